@@ -1,0 +1,36 @@
+/*
+ * hbm_probe.h - plain streaming kernels that measure what HBM delivers on the
+ * device they run on, for comparison with the activation kernels.
+ *
+ * hbm_probe_stream reads n_src arrays and writes n_dst arrays of n_vec 16-byte
+ * vectors each: every destination vector becomes the XOR of the source vectors at
+ * the same index (a plain copy for n_src = n_dst = 1). Ratios 1:1, 2:1 and 3:2
+ * mirror a copy, the activation forward (gate + up -> y) and its backward
+ * (gate + up + grad_y -> two halves of grad_x). The kernel moves exactly
+ * (n_src + n_dst) * n_vec * 16 bytes, so it also calibrates the hardware byte
+ * counters (FETCH_SIZE / WRITE_SIZE) against a known size.
+ *
+ * Pointers: device memory on the current HIP device, 16-byte aligned, caller-owned,
+ * destinations must not overlap sources. 1 <= n_src <= 3, 1 <= n_dst <= 2.
+ * num_workgroups = 0 picks CUs x resident workgroups per CU. Work is enqueued on
+ * `stream`; no synchronisation, no allocation.
+ * Returns 0 on success, 1 for invalid arguments, 3 when the launch failed.
+ */
+#ifndef HBM_PROBE_H
+#define HBM_PROBE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int hbm_probe_stream(const void *const *src, int n_src, void *const *dst, int n_dst,
+                     int64_t n_vec, int num_workgroups, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HBM_PROBE_H */

@@ -1,0 +1,591 @@
+// Fused clamped-SwiGLU x routing-probability activation, forward and backward,
+// for AMD Instinct MI355X (gfx950, CDNA4). C ABI declared in swiglu_probs.h.
+//
+// What is computed (NeMo AutoModel "moe/swiglu_triton" page, module docstring):
+//   y = silu(clamp(gate, max=L)) * clamp(up, -L, L) * probs, fp32 math, one bf16
+//   rounding; the backward writes d_gate / d_up into the two halves of grad_x and
+//   reduces the per-row probability gradient in fp32. Clamp gradients follow
+//   torch.clamp (inclusive masks). Row bookkeeping (n_used, permutation_map,
+//   zero_padding, fixed grid striding over rows) follows the Megatron-Core
+//   "core.inference.moe.batch_invariant" page (_swiglu_with_probs_kernel,
+//   _weighted_silu_mul_bounded_kernel).
+//
+// Design (HBM-bound; no MFMA):
+//   * One wavefront (64 lanes) owns one row at a time. Lane l handles the 16-byte
+//     vectors l, l+64, l+128, ... of the gate half, the up half and (backward)
+//     grad_y: every load and store is a 128-bit access and a wave instruction
+//     covers 1 KiB of contiguous memory.
+//   * All loads of a chunk (U vectors per lane per stream) are issued before any
+//     arithmetic, so a wave keeps up to 3*U*1 KiB in flight.
+//   * Waves stride over rows with a fixed grid (row r, r + W, r + 2W, ...), so the
+//     launch never depends on device data and is graph-safe; the grid is sized so
+//     every wave gets the same number of rows.
+//   * Per-row metadata (permutation slot and probability) for a wave's next 64
+//     rows is gathered with one vector load, one row per lane, and broadcast with
+//     v_readlane when the row is processed: no per-row dependent scalar loads.
+//   * The probability gradient: each lane sums its own columns in a fixed order,
+//     then a butterfly over the wave (DPP quad/row permutes, then two lane
+//     exchanges) combines the 64 partials. The order depends only on the column to
+//     lane mapping, never on the grid, so the bits are grid-invariant.
+//   * fp32 -> bf16 uses v_cvt_pk_bf16_f32 (round to nearest even, two values per
+//     instruction); the clamps use v_minimum3/v_maximum3 (NaN-propagating, as
+//     torch.clamp); the inclusive masks are "the clamp left the value unchanged".
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "swiglu_probs.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kMaxU = 4;  // 16-byte vectors per lane per stream per chunk
+constexpr float kNegLog2e = -1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Element math
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+// clamp(gate, max=L) and clamp(up, -L, L); NaN propagates like torch.clamp.
+__device__ __forceinline__ float clamp_gate(float a, float L)
+{
+    return __builtin_elementwise_minimum(a, L);
+}
+__device__ __forceinline__ float clamp_up(float b, float L)
+{
+    return __builtin_elementwise_maximum(__builtin_elementwise_minimum(b, L), -L);
+}
+
+// logistic sigmoid 1 / (1 + e^-z) from v_exp_f32 (2^x) and v_rcp_f32.
+// v_rcp_f32 flushes subnormal results to zero, and 1 / (1 + e^-z) is subnormal once
+// 1 + e^-z exceeds 2^126 (z < -87.3), where silu(z) = z * sigmoid(z) is still a normal
+// number. The reciprocal is therefore taken of 2^-64 * (1 + e^-z) (one fma, exact: a
+// power-of-two scale of a value >= 1), which keeps it normal, and the result is scaled
+// back by 2^-64 in a multiply, which does produce subnormals. For e^-z = inf (z < -88.7)
+// the sigmoid is 0, as 1 / (1 + inf) is in fp32.
+__device__ __forceinline__ float sigmoid(float z)
+{
+    constexpr float kTwoM64 = 0x1p-64f;
+    float e = __builtin_amdgcn_exp2f(z * kNegLog2e);
+    return __builtin_amdgcn_rcpf(__builtin_fmaf(e, kTwoM64, kTwoM64)) * kTwoM64;
+}
+
+__device__ __forceinline__ float fwd_elem(float a, float b, float p, float L)
+{
+    float cg = clamp_gate(a, L);
+    float cu = clamp_up(b, L);
+    float s = cg * sigmoid(cg);
+    return (s * cu) * p;
+}
+
+// Autograd chain of y = (silu(cg) * cu) * p with inclusive clamp masks.
+__device__ __forceinline__ void bwd_elem(float a, float b, float g, float p, float L,
+                                         float &dg, float &du, float &acc)
+{
+    float cg = clamp_gate(a, L);
+    float cu = clamp_up(b, L);
+    float sig = sigmoid(cg);
+    float s = cg * sig;
+    float gp = g * p;
+    float dsilu = sig * (1.0f + cg * (1.0f - sig));
+    // a <= L  <=>  min(a, L) == a ;  -L <= b <= L  <=>  clamp(b) == b  (false for NaN)
+    dg = (cg == a) ? (gp * cu) * dsilu : 0.0f;
+    du = (cu == b) ? gp * s : 0.0f;
+    acc += g * (s * cu);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide sum with a fixed combination order; every lane ends with the total.
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lanes ^1
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lanes ^2
+    v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8
+    v += dpp<0x140>(v);  // row_mirror: the other half of each 16
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Row schedule shared by both kernels
+// ---------------------------------------------------------------------------
+struct RowSchedule {
+    int rows;     // rows of every row-indexed tensor (max_rows)
+    int live;     // clamp(*n_used, 0, rows), or rows
+    int row_end;  // rows this launch visits: rows with zero_padding, else live
+};
+
+__device__ __forceinline__ RowSchedule make_schedule(int rows, const int *__restrict__ n_used,
+                                                     int zero_padding)
+{
+    RowSchedule s;
+    s.rows = rows;
+    s.live = rows;
+    if (n_used) {
+        int n = *n_used;
+        s.live = n < 0 ? 0 : (n > rows ? rows : n);
+    }
+    s.row_end = zero_padding ? rows : s.live;
+    return s;
+}
+
+// Gathers (slot, probability) of row `ri` for the calling lane; slot -1 = not live.
+__device__ __forceinline__ void row_meta(int64_t ri, const RowSchedule &s, const int *__restrict__ perm,
+                                         const float *__restrict__ probs, int &slot, float &p)
+{
+    slot = -1;
+    p = 0.0f;
+    if (ri < s.live) {
+        int v = perm ? perm[ri] : (int)ri;
+        if ((unsigned)v < (unsigned)s.rows) {
+            slot = v;
+            p = probs[v];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward kernel
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
+    const u32x4 *__restrict__ x, const float *__restrict__ probs, u32x4 *__restrict__ y,
+    int rows, int vpr, float L, const int *__restrict__ n_used, const int *__restrict__ perm,
+    int zero_padding)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int W = gridDim.x * kWavesPerBlock;
+    const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+
+    for (int64_t base = w; base < sched.row_end; base += (int64_t)kWave * W) {
+        int slot_l;
+        float p_l;
+        row_meta(base + (int64_t)lane * W, sched, perm, probs, slot_l, p_l);
+        const int64_t left = (sched.row_end - base + W - 1) / W;
+        const int nk = left < kWave ? (int)left : kWave;
+
+        for (int k = 0; k < nk; ++k) {
+            const int64_t r = base + (int64_t)k * W;
+            const int slot = __builtin_amdgcn_readlane(slot_l, k);
+            u32x4 *__restrict__ yr = y + r * vpr;
+            if (slot >= 0) {
+                const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
+                const u32x4 *__restrict__ gr = x + r * 2 * vpr;
+                const u32x4 *__restrict__ ur = gr + vpr;
+                for (int c0 = 0; c0 < vpr; c0 += kWave * U) {
+                    u32x4 G[U], V[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = c0 + u * kWave + lane;
+                        if (v < vpr) {
+                            G[u] = gr[v];
+                            V[u] = ur[v];
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = c0 + u * kWave + lane;
+                        if (v < vpr) {
+                            u32x4 o;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                float y0 = fwd_elem(bf16_lo(G[u][q]), bf16_lo(V[u][q]), p, L);
+                                float y1 = fwd_elem(bf16_hi(G[u][q]), bf16_hi(V[u][q]), p, L);
+                                o[q] = pack_bf16x2(y0, y1);
+                            }
+                            yr[v] = o;
+                        }
+                    }
+                }
+            } else if (zero_padding) {
+                for (int v = lane; v < vpr; v += kWave)
+                    yr[v] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward kernel
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_kernel(
+    const u32x4 *__restrict__ x, const float *__restrict__ probs, const u32x4 *__restrict__ gy,
+    u32x4 *__restrict__ gx, float *__restrict__ gprobs, int rows, int vpr, float L,
+    const int *__restrict__ n_used, const int *__restrict__ perm, int zero_padding)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int W = gridDim.x * kWavesPerBlock;
+    const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+
+    for (int64_t base = w; base < sched.row_end; base += (int64_t)kWave * W) {
+        int slot_l;
+        float p_l;
+        row_meta(base + (int64_t)lane * W, sched, perm, probs, slot_l, p_l);
+        const int64_t left = (sched.row_end - base + W - 1) / W;
+        const int nk = left < kWave ? (int)left : kWave;
+
+        for (int k = 0; k < nk; ++k) {
+            const int64_t r = base + (int64_t)k * W;
+            const int slot = __builtin_amdgcn_readlane(slot_l, k);
+            u32x4 *__restrict__ dgr = gx + r * 2 * vpr;
+            u32x4 *__restrict__ dur = dgr + vpr;
+            if (slot >= 0) {
+                const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
+                const u32x4 *__restrict__ gr = x + r * 2 * vpr;
+                const u32x4 *__restrict__ ur = gr + vpr;
+                const u32x4 *__restrict__ yr = gy + r * vpr;
+                float acc = 0.0f;
+                for (int c0 = 0; c0 < vpr; c0 += kWave * U) {
+                    u32x4 G[U], V[U], Y[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = c0 + u * kWave + lane;
+                        if (v < vpr) {
+                            G[u] = gr[v];
+                            V[u] = ur[v];
+                            Y[u] = yr[v];
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = c0 + u * kWave + lane;
+                        if (v < vpr) {
+                            u32x4 og, ou;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                float dg0, du0, dg1, du1;
+                                bwd_elem(bf16_lo(G[u][q]), bf16_lo(V[u][q]), bf16_lo(Y[u][q]), p, L,
+                                         dg0, du0, acc);
+                                bwd_elem(bf16_hi(G[u][q]), bf16_hi(V[u][q]), bf16_hi(Y[u][q]), p, L,
+                                         dg1, du1, acc);
+                                og[q] = pack_bf16x2(dg0, dg1);
+                                ou[q] = pack_bf16x2(du0, du1);
+                            }
+                            dgr[v] = og;
+                            dur[v] = ou;
+                        }
+                    }
+                }
+                const float total = wave_sum(acc);
+                if (gprobs && lane == 0)
+                    gprobs[slot] = total;
+            } else if (zero_padding) {
+                for (int v = lane; v < 2 * vpr; v += kWave)
+                    dgr[v] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, launch configuration
+// ---------------------------------------------------------------------------
+thread_local int t_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceLaunchInfo {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    int cus = 0;
+    int fwd_blocks_per_cu[kMaxU + 1] = {};
+    int bwd_blocks_per_cu[kMaxU + 1] = {};
+};
+DeviceLaunchInfo g_devices[kMaxDevices];
+
+template <int U>
+hipError_t occupancy(int *fwd, int *bwd)
+{
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        fwd, reinterpret_cast<const void *>(swiglu_probs_fwd_kernel<U>), kBlock, 0);
+    if (e != hipSuccess)
+        return e;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        bwd, reinterpret_cast<const void *>(swiglu_probs_bwd_kernel<U>), kBlock, 0);
+}
+
+void init_device(int dev, DeviceLaunchInfo &info)
+{
+    hipDeviceProp_t prop;
+    info.err = hipGetDeviceProperties(&prop, dev);
+    if (info.err != hipSuccess)
+        return;
+    info.cus = prop.multiProcessorCount;
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = occupancy<1>(&info.fwd_blocks_per_cu[1], &info.bwd_blocks_per_cu[1]);
+    if (e == hipSuccess) e = occupancy<2>(&info.fwd_blocks_per_cu[2], &info.bwd_blocks_per_cu[2]);
+    if (e == hipSuccess) e = occupancy<3>(&info.fwd_blocks_per_cu[3], &info.bwd_blocks_per_cu[3]);
+    if (e == hipSuccess) e = occupancy<4>(&info.fwd_blocks_per_cu[4], &info.bwd_blocks_per_cu[4]);
+    info.err = e;
+}
+
+hipError_t device_info(DeviceLaunchInfo **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    DeviceLaunchInfo &info = g_devices[dev];
+    std::call_once(info.once, init_device, dev, std::ref(info));
+    *out = &info;
+    return info.err;
+}
+
+int pick_u(int64_t vpr)
+{
+    int64_t u = (vpr + kWave - 1) / kWave;
+    return u >= kMaxU ? kMaxU : (u < 1 ? 1 : (int)u);
+}
+
+// Workgroups so that the resident waves divide the rows evenly: with R rows and at
+// most M resident waves, rounds = ceil(R / M) and W = ceil(R / rounds) waves.
+int balanced_workgroups(int64_t rows, int cus, int blocks_per_cu)
+{
+    if (blocks_per_cu < 1)
+        blocks_per_cu = 1;
+    const int64_t max_waves = (int64_t)cus * blocks_per_cu * kWavesPerBlock;
+    if (rows <= 0)
+        return 1;
+    const int64_t rounds = (rows + max_waves - 1) / max_waves;
+    const int64_t waves = (rows + rounds - 1) / rounds;
+    return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b)
+{
+    if (a.lo == a.hi || b.lo == b.hi)
+        return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+Range range_of(const void *p, uint64_t bytes)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, p ? lo + (uintptr_t)bytes : lo};
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxRows = 0x7fffffffLL - 64LL * 65536LL;  // row indices stay in int32
+constexpr int64_t kMaxInter = 1LL << 28;
+
+swiglu_status_t check_shape(int64_t rows, int64_t inter, float limit, int num_workgroups)
+{
+    if (rows < 0 || inter <= 0 || rows > kMaxRows || inter > kMaxInter)
+        return SWIGLU_ERR_INVALID_ARG;
+    if ((uint64_t)rows * (uint64_t)inter > (1ULL << 60))
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!(limit > 0.0f))  // NaN or <= 0; +inf is allowed (no clamp)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (num_workgroups < 0)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (inter % 8 != 0)
+        return SWIGLU_ERR_ALIGNMENT;
+    return SWIGLU_OK;
+}
+
+swiglu_status_t fail_hip(hipError_t e)
+{
+    t_last_hip_error = (int)e;
+    return SWIGLU_ERR_HIP;
+}
+
+template <int U>
+void launch_fwd(int blocks, hipStream_t stream, const uint16_t *x, const float *probs, uint16_t *y,
+                int rows, int vpr, float limit, const int32_t *n_used, const int32_t *perm, int zp)
+{
+    hipLaunchKernelGGL(swiglu_probs_fwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream,
+                       reinterpret_cast<const u32x4 *>(x), probs, reinterpret_cast<u32x4 *>(y), rows,
+                       vpr, limit, n_used, perm, zp);
+}
+
+template <int U>
+void launch_bwd(int blocks, hipStream_t stream, const uint16_t *x, const float *probs,
+                const uint16_t *gy, uint16_t *gx, float *gp, int rows, int vpr, float limit,
+                const int32_t *n_used, const int32_t *perm, int zp)
+{
+    hipLaunchKernelGGL(swiglu_probs_bwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream,
+                       reinterpret_cast<const u32x4 *>(x), probs, reinterpret_cast<const u32x4 *>(gy),
+                       reinterpret_cast<u32x4 *>(gx), gp, rows, vpr, limit, n_used, perm, zp);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint16_t *y,
+                                    int64_t rows, int64_t inter, float limit,
+                                    const int32_t *n_used, const int32_t *permutation_map,
+                                    int zero_padding, hipStream_t stream, int num_workgroups)
+{
+    swiglu_status_t st = check_shape(rows, inter, limit, num_workgroups);
+    if (st != SWIGLU_OK)
+        return st;
+    if (rows == 0)
+        return SWIGLU_OK;
+    if (!x || !probs || !y)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(probs, 4) || !aligned(n_used, 4) ||
+        !aligned(permutation_map, 4))
+        return SWIGLU_ERR_ALIGNMENT;
+    const uint64_t R = (uint64_t)rows, I = (uint64_t)inter;
+    const Range out = range_of(y, R * I * 2);
+    const Range ins[] = {range_of(x, R * I * 4), range_of(probs, R * 4), range_of(n_used, 4),
+                         range_of(permutation_map, R * 4)};
+    for (const Range &in : ins)
+        if (overlaps(out, in))
+            return SWIGLU_ERR_INVALID_ARG;
+
+    DeviceLaunchInfo *info = nullptr;
+    hipError_t e = device_info(&info);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    const int vpr = (int)(inter / 8);
+    const int U = pick_u(vpr);
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : balanced_workgroups(rows, info->cus, info->fwd_blocks_per_cu[U]);
+    const int zp = zero_padding ? 1 : 0;
+    switch (U) {
+    case 1: launch_fwd<1>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    case 2: launch_fwd<2>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    case 3: launch_fwd<3>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    default: launch_fwd<4>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail_hip(e);
+    return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                    uint16_t *grad_x, float *grad_probs,
+                                    int64_t rows, int64_t inter, float limit,
+                                    const int32_t *n_used, const int32_t *permutation_map,
+                                    int zero_padding, hipStream_t stream, int num_workgroups)
+{
+    swiglu_status_t st = check_shape(rows, inter, limit, num_workgroups);
+    if (st != SWIGLU_OK)
+        return st;
+    if (rows == 0)
+        return SWIGLU_OK;
+    if (!x || !probs || !grad_y || !grad_x)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(grad_y, 16) || !aligned(grad_x, 16) || !aligned(probs, 4) ||
+        !aligned(grad_probs, 4) || !aligned(n_used, 4) || !aligned(permutation_map, 4))
+        return SWIGLU_ERR_ALIGNMENT;
+    const uint64_t R = (uint64_t)rows, I = (uint64_t)inter;
+    const Range outs[] = {range_of(grad_x, R * I * 4), range_of(grad_probs, R * 4)};
+    const Range ins[] = {range_of(x, R * I * 4), range_of(probs, R * 4), range_of(grad_y, R * I * 2),
+                         range_of(n_used, 4), range_of(permutation_map, R * 4)};
+    for (const Range &o : outs)
+        for (const Range &in : ins)
+            if (overlaps(o, in))
+                return SWIGLU_ERR_INVALID_ARG;
+    if (overlaps(outs[0], outs[1]))
+        return SWIGLU_ERR_INVALID_ARG;
+
+    DeviceLaunchInfo *info = nullptr;
+    hipError_t e = device_info(&info);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    const int vpr = (int)(inter / 8);
+    const int U = pick_u(vpr);
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : balanced_workgroups(rows, info->cus, info->bwd_blocks_per_cu[U]);
+    const int zp = zero_padding ? 1 : 0;
+    switch (U) {
+    case 1: launch_bwd<1>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    case 2: launch_bwd<2>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    case 3: launch_bwd<3>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    default: launch_bwd<4>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail_hip(e);
+    return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_probs_fwd(const uint16_t *x, const float *probs, uint16_t *y,
+                                 int64_t rows, int64_t inter, float limit,
+                                 const int32_t *n_used, const int32_t *permutation_map,
+                                 int zero_padding, hipStream_t stream)
+{
+    return swiglu_probs_fwd_ex(x, probs, y, rows, inter, limit, n_used, permutation_map,
+                               zero_padding, stream, 0);
+}
+
+swiglu_status_t swiglu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                 uint16_t *grad_x, float *grad_probs,
+                                 int64_t rows, int64_t inter, float limit,
+                                 const int32_t *n_used, const int32_t *permutation_map,
+                                 int zero_padding, hipStream_t stream)
+{
+    return swiglu_probs_bwd_ex(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, n_used,
+                               permutation_map, zero_padding, stream, 0);
+}
+
+int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter)
+{
+    if (rows < 0 || inter <= 0 || inter % 8 != 0 || (direction != 0 && direction != 1))
+        return -1;
+    DeviceLaunchInfo *info = nullptr;
+    if (device_info(&info) != hipSuccess)
+        return -1;
+    const int U = pick_u(inter / 8);
+    const int bpc = direction == 0 ? info->fwd_blocks_per_cu[U] : info->bwd_blocks_per_cu[U];
+    return balanced_workgroups(rows, info->cus, bpc);
+}
+
+const char *swiglu_probs_status_string(swiglu_status_t status)
+{
+    switch (status) {
+    case SWIGLU_OK: return "ok";
+    case SWIGLU_ERR_INVALID_ARG: return "invalid argument";
+    case SWIGLU_ERR_ALIGNMENT: return "misaligned pointer or inter not a multiple of 8";
+    case SWIGLU_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int swiglu_probs_last_hip_error(void) { return t_last_hip_error; }
+
+int swiglu_probs_abi_version(void) { return SWIGLU_PROBS_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+"""The C ABI libraries load on the host and export every symbol their headers
+declare; argument validation rejects bad calls before anything reaches HIP.
+
+No kernel is launched here (no GPU in this environment): every call below fails
+validation, or has rows == 0, and returns before the first HIP runtime call.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from memory_bound_elementwise_amd import build as mbuild
+from memory_bound_elementwise_amd import load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_TO_LIB = {"swiglu_probs.h": "swiglu_probs", "hbm_probe.h": "hbm_probe"}
+
+
+def declared_functions(header: str):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*\b([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def built():
+    for name in HEADER_TO_LIB.values():
+        if not os.path.exists(mbuild.lib_path(name)):
+            mbuild.build_lib(name)
+
+
+def test_every_header_is_mapped():
+    heads = sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert heads == sorted(HEADER_TO_LIB)
+
+
+@pytest.mark.parametrize("header,lib", sorted(HEADER_TO_LIB.items()))
+def test_library_exports_declared_symbols(built, header, lib):
+    names = declared_functions(os.path.join(ROOT, "include", header))
+    assert names, f"no declarations parsed from {header}"
+    so = ctypes.CDLL(mbuild.lib_path(lib))
+    missing = [n for n in names if not hasattr(so, n)]
+    assert not missing, f"{lib} does not export {missing}"
+    nm = subprocess.run(["nm", "-D", "--defined-only", mbuild.lib_path(lib)],
+                        capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), f"{n} not a defined text symbol"
+
+
+def test_swiglu_declarations_expected():
+    names = declared_functions(os.path.join(ROOT, "include", "swiglu_probs.h"))
+    for n in ("swiglu_probs_fwd", "swiglu_probs_bwd", "swiglu_probs_fwd_ex", "swiglu_probs_bwd_ex",
+              "swiglu_probs_status_string", "swiglu_probs_abi_version",
+              "swiglu_probs_last_hip_error", "swiglu_probs_default_workgroups"):
+        assert n in names
+
+
+A16 = 1 << 20  # a 16-byte aligned fake address; never dereferenced on these paths
+
+
+def fwd(lib, x=A16, probs=A16 + (1 << 24), y=A16 + (2 << 24), rows=4, inter=8, limit=7.0,
+        n_used=None, perm=None, zp=0, nwg=0):
+    return lib.swiglu_probs_fwd_ex(x, probs, y, rows, inter, limit, n_used, perm, zp, None, nwg)
+
+
+def bwd(lib, x=A16, probs=A16 + (1 << 24), gy=A16 + (2 << 24), gx=A16 + (3 << 24),
+        gp=A16 + (4 << 24), rows=4, inter=8, limit=7.0, n_used=None, perm=None, zp=0, nwg=0):
+    return lib.swiglu_probs_bwd_ex(x, probs, gy, gx, gp, rows, inter, limit, n_used, perm, zp,
+                                   None, nwg)
+
+
+def test_validation_fwd():
+    lib = load_library()
+    assert fwd(lib, rows=0) == 0                       # empty: no launch
+    assert fwd(lib, rows=0, x=None, y=None, probs=None) == 0
+    assert fwd(lib, rows=-1) == 1
+    assert fwd(lib, inter=0) == 1
+    assert fwd(lib, inter=-8) == 1
+    assert fwd(lib, inter=12) == 2                     # not a multiple of 8
+    assert fwd(lib, limit=float("nan")) == 1
+    assert fwd(lib, limit=0.0) == 1
+    assert fwd(lib, limit=-7.0) == 1
+    assert fwd(lib, nwg=-1) == 1
+    assert fwd(lib, x=None) == 1
+    assert fwd(lib, probs=None) == 1
+    assert fwd(lib, y=None) == 1
+    assert fwd(lib, x=A16 + 8) == 2
+    assert fwd(lib, y=A16 + (2 << 24) + 2) == 2
+    assert fwd(lib, probs=A16 + (1 << 24) + 2) == 2
+    assert fwd(lib, n_used=A16 + (5 << 24) + 1) == 2
+    assert fwd(lib, perm=A16 + (6 << 24) + 3) == 2
+    assert fwd(lib, y=A16 + 16) == 1                    # y overlaps x
+    assert fwd(lib, y=A16 + (1 << 24)) == 1             # y overlaps probs
+    assert fwd(lib, rows=1 << 40) == 1                  # too many rows
+    assert fwd(lib, inter=1 << 40) == 1
+
+
+def test_validation_bwd():
+    lib = load_library()
+    assert bwd(lib, rows=0) == 0
+    assert bwd(lib, rows=-3) == 1
+    assert bwd(lib, inter=20) == 2
+    assert bwd(lib, limit=float("nan")) == 1
+    assert bwd(lib, x=None) == 1
+    assert bwd(lib, gy=None) == 1
+    assert bwd(lib, gx=None) == 1
+    assert bwd(lib, probs=None) == 1
+    assert bwd(lib, gp=A16 + (4 << 24) + 1) == 2
+    assert bwd(lib, gx=A16 + (3 << 24) + 4) == 2
+    assert bwd(lib, gx=A16) == 1                        # grad_x over x
+    assert bwd(lib, gx=A16 + (2 << 24)) == 1            # grad_x over grad_y
+    assert bwd(lib, gp=A16 + (1 << 24)) == 1            # grad_probs over probs
+    assert bwd(lib, gp=A16 + (3 << 24) + 16) == 1       # grad_probs inside grad_x
+    assert bwd(lib, perm=A16 + (3 << 24)) == 1          # map overlaps an output
+
+
+def test_status_strings_and_version():
+    lib = load_library()
+    assert lib.swiglu_probs_abi_version() == 1
+    for st in range(4):
+        assert lib.swiglu_probs_status_string(st)
+    assert lib.swiglu_probs_status_string(99) == b"unknown status"
+
+
+def test_probe_validation(built):
+    so = ctypes.CDLL(mbuild.lib_path("hbm_probe"))
+    so.hbm_probe_stream.restype = ctypes.c_int
+    so.hbm_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    s = (ctypes.c_void_p * 1)(A16)
+    d = (ctypes.c_void_p * 1)(A16 + (1 << 24))
+    assert so.hbm_probe_stream(s, 1, d, 1, 0, 0, None) == 0
+    assert so.hbm_probe_stream(s, 0, d, 1, 4, 0, None) == 1
+    assert so.hbm_probe_stream(s, 1, d, 3, 4, 0, None) == 1
+    d2 = (ctypes.c_void_p * 1)(A16 + 16)
+    assert so.hbm_probe_stream(s, 1, d2, 1, 4, 0, None) == 1   # overlap

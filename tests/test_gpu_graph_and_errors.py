@@ -1,0 +1,109 @@
+"""hipGraph capture/replay with a device-side n_used, the autograd wrapper, and the
+C ABI's error paths on real device pointers."""
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_elementwise_amd import (SwigluProbs, SwigluProbsError, load_library,
+                                          swiglu_probs_bwd, swiglu_probs_fwd)
+from memory_bound_elementwise_amd.workloads import make_inputs
+from parity import (compare_grad_probs, compare_rows, live_mask, run_oracle, say,
+                    to_dev_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_follows_device_n_used():
+    """Capture one forward and one backward; change the device n_used between
+    replays; every replay matches the oracle for the count it saw."""
+    dev = torch.device("cuda:0")
+    inp = make_inputs("padded", seed=7, rows=8192)
+    rows, two_inter = inp["x"].shape
+    x = to_dev_bits(inp["x"], dev)
+    gy = to_dev_bits(inp["grad_y"], dev)
+    probs = torch.from_numpy(inp["probs"]).to(dev)
+    pm = torch.from_numpy(inp["permutation_map"]).to(dev)
+    n_used = torch.tensor([inp["n_used"]], dtype=torch.int32, device=dev)
+    y = torch.empty((rows, two_inter // 2), dtype=torch.int16, device=dev)
+    gx = torch.empty((rows, two_inter), dtype=torch.int16, device=dev)
+    gp = torch.empty((rows,), dtype=torch.float32, device=dev)
+    kw = dict(n_used=n_used, permutation_map=pm, zero_padding=True)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside the capture (launch info cached)
+        swiglu_probs_fwd(x, probs, y, inp["limit"], **kw)
+        swiglu_probs_bwd(x, probs, gy, gx, gp, inp["limit"], **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        swiglu_probs_fwd(x, probs, y, inp["limit"], **kw)
+        swiglu_probs_bwd(x, probs, gy, gx, gp, inp["limit"], **kw)
+
+    for count in (inp["n_used"], 5000, 8192, 1, inp["n_used"]):
+        say(f"[graph] replay with n_used={count}")
+        n_used.fill_(count)                   # eager work between replays
+        y.fill_(-1)
+        gx.fill_(-1)
+        gp.fill_(-12345.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        case = dict(inp, n_used=count)
+        ry, rout = run_oracle(case)
+        live = live_mask(case)
+        inter = two_inter // 2
+        compare_rows(y.cpu().numpy().view(np.uint16), ry, live, f"graph y n_used={count}")
+        gxn = gx.cpu().numpy().view(np.uint16)
+        compare_rows(gxn[:, :inter], rout["grad_x"][:, :inter], live, "graph d_gate")
+        compare_rows(gxn[:, inter:], rout["grad_x"][:, inter:], live, "graph d_up")
+        compare_grad_probs(gp.cpu().numpy(), rout, case, "graph grad_probs")
+
+
+def test_autograd_function_matches_oracle():
+    dev = torch.device("cuda:0")
+    inp = make_inputs("tiny", seed=8)
+    x = to_dev_bits(inp["x"], dev).view(torch.bfloat16).requires_grad_(True)
+    probs = torch.from_numpy(inp["probs"]).to(dev).reshape(-1, 1).requires_grad_(True)
+    gy = to_dev_bits(inp["grad_y"], dev).view(torch.bfloat16)
+    y = SwigluProbs.apply(x, probs, inp["limit"])
+    y.backward(gy)
+    ry, rout = run_oracle(inp)
+    live = np.ones(x.shape[0], dtype=bool)
+    compare_rows(y.detach().view(torch.int16).cpu().numpy().view(np.uint16), ry, live, "autograd y")
+    compare_rows(x.grad.view(torch.int16).cpu().numpy().view(np.uint16), rout["grad_x"], live,
+                 "autograd grad_x")
+    assert probs.grad.shape == probs.shape
+    compare_grad_probs(probs.grad.reshape(-1).cpu().numpy(), rout, inp, "autograd grad_probs")
+
+
+def test_error_paths_write_nothing():
+    dev = torch.device("cuda:0")
+    lib = load_library()
+    rows, inter = 64, 64
+    x = torch.zeros((rows, 2 * inter), dtype=torch.int16, device=dev)
+    probs = torch.zeros(rows, dtype=torch.float32, device=dev)
+    y = torch.full((rows, inter), 77, dtype=torch.int16, device=dev)
+    # misaligned x (by one bf16)
+    st = lib.swiglu_probs_fwd(x.data_ptr() + 2, probs.data_ptr(), y.data_ptr(), rows - 1, inter,
+                              7.0, None, None, 0, None)
+    assert st == 2
+    # y overlapping x
+    st = lib.swiglu_probs_fwd(x.data_ptr(), probs.data_ptr(), x.data_ptr() + 16 * 64, rows, inter,
+                              7.0, None, None, 0, None)
+    assert st == 1
+    # limit NaN / zero / negative
+    for bad in (float("nan"), 0.0, -1.0):
+        assert lib.swiglu_probs_fwd(x.data_ptr(), probs.data_ptr(), y.data_ptr(), rows, inter, bad,
+                                    None, None, 0, None) == 1
+    torch.cuda.synchronize()
+    assert torch.all(y == 77), "an invalid call wrote to its output"
+    with pytest.raises(SwigluProbsError):
+        swiglu_probs_fwd(x, probs, y, float("nan"))
+    with pytest.raises(ValueError):
+        swiglu_probs_fwd(x, probs[:-1], y, 7.0)
+    # rows == 0 is a no-op that launches nothing
+    assert lib.swiglu_probs_bwd(None, None, None, None, None, 0, 8, 7.0, None, None, 0, None) == 0
+    assert lib.swiglu_probs_last_hip_error() == 0

@@ -1,0 +1,99 @@
+"""HIP path vs CPU oracle, element by element, on the five seeded workloads and on
+reduced copies that span several row rounds with a ragged tail.
+
+All calls go through the C ABI (ctypes binding). Bar: see ``parity.py``.
+"""
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_elementwise_amd import swiglu_probs_default_workgroups
+from memory_bound_elementwise_amd.workloads import WORKLOADS, make_inputs
+from parity import check_parity, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "headline", "padded", "edge"])
+def test_workload_parity_full_size(name):
+    """Every output element of the full-size workload, in the launch the bench times."""
+    inp = make_inputs(name, seed=0)
+    check_parity(inp, label=f"{name} full")
+
+
+@pytest.mark.parametrize("name,rows", [("mid", 1021), ("edge", 4099), ("padded", 3001),
+                                       ("headline", 517), ("tiny", 1)])
+def test_workload_parity_reduced(name, rows):
+    inp = make_inputs(name, seed=1, rows=rows)
+    check_parity(inp, label=f"{name} rows={rows}")
+
+
+@pytest.mark.parametrize("inter", [8, 16, 24, 64, 512, 520, 1400, 2056, 4096, 8192 + 8])
+def test_odd_widths(inter):
+    """Widths that leave lanes idle, need several column chunks, or end mid-chunk."""
+    from memory_bound_elementwise_amd.workloads import Workload
+    w = Workload("odd", rows=333, inter=inter, limit=3.0, x_std=3.0)
+    check_parity(make_inputs(w, seed=inter), label=f"inter={inter}")
+
+
+def test_grid_invariance_and_determinism():
+    """Result bits do not depend on the workgroup count or on the run."""
+    inp = make_inputs("edge", seed=2, rows=3000)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ref = run_gpu(inp)
+    for nwg in (1, 3, cus, 4 * cus, 10 * cus, 0):
+        say(f"[grid] workgroups={nwg}")
+        got = run_gpu(inp, num_workgroups=nwg)
+        for a, b, what in zip(got, ref, ("y", "grad_x", "grad_probs")):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{what} bits changed with {nwg} workgroups"
+
+
+def test_row_subset_invariance():
+    """A row's bits do not depend on the other rows in the launch (batch invariance)."""
+    full = make_inputs("mid", seed=3, rows=600)
+    ref = run_gpu(full)
+    sub = np.arange(100, 357)
+    part = dict(full, x=full["x"][sub], probs=full["probs"][sub], grad_y=full["grad_y"][sub])
+    got = run_gpu(part)
+    assert np.array_equal(got[0], ref[0][sub])
+    assert np.array_equal(got[1], ref[1][sub])
+    assert np.array_equal(got[2].view(np.uint32), ref[2][sub].view(np.uint32))
+
+
+def test_no_grad_probs_pointer():
+    """grad_probs = NULL skips the reduction and leaves grad_x unchanged."""
+    inp = make_inputs("tiny", seed=4)
+    _, gx_ref, _ = run_gpu(inp, do_fwd=False)
+    _, gx, gp = run_gpu(inp, do_fwd=False, grad_probs=False)
+    assert gp is None and np.array_equal(gx, gx_ref)
+
+
+@pytest.mark.parametrize("n_used", [0, 1, 29999, 30000, 32768, 40000, -7])
+def test_padded_n_used_values(n_used):
+    inp = make_inputs("padded", seed=5, rows=4096)
+    inp["n_used"] = n_used
+    check_parity(inp, label=f"padded n_used={n_used}")
+
+
+@pytest.mark.parametrize("zero_padding", [False, True])
+def test_dummy_map_entries(zero_padding):
+    """Map entries outside [0, rows) mark interior dummy rows."""
+    inp = make_inputs("padded", seed=6, rows=2048)
+    pm = inp["permutation_map"].copy()
+    rng = np.random.default_rng(0)
+    dummy = rng.choice(2048, size=100, replace=False)
+    pm[dummy[:50]] = -1
+    pm[dummy[50:]] = 2048 + rng.integers(0, 1000, size=50)
+    inp["permutation_map"] = pm
+    inp["zero_padding"] = zero_padding
+    check_parity(inp, label=f"dummy entries zero_padding={zero_padding}")
+
+
+def test_default_workgroups_balanced():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for d in ("fwd", "bwd"):
+        wg = swiglu_probs_default_workgroups(d, WORKLOADS["headline"].rows, WORKLOADS["headline"].inter)
+        waves = wg * 4
+        rounds = -(-WORKLOADS["headline"].rows // waves)
+        say(f"[launch] {d}: {wg} workgroups on {cus} CUs, {rounds} row rounds")
+        assert wg >= cus and rounds * waves - WORKLOADS["headline"].rows < waves

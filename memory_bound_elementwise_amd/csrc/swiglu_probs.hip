@@ -13,13 +13,21 @@
 // Design (HBM-bound; no MFMA):
 //   * One wavefront (64 lanes) owns one row at a time. Lane l handles the 16-byte
 //     vectors l, l+64, l+128, ... of the gate half, the up half and (backward)
-//     grad_y: every load and store is a 128-bit access and a wave instruction
-//     covers 1 KiB of contiguous memory.
-//   * All loads of a chunk (U vectors per lane per stream) are issued before any
-//     arithmetic, so a wave keeps up to 3*U*1 KiB in flight.
+//     grad_y: every access is 128 bits wide and one wave instruction covers 1 KiB
+//     of contiguous memory. A row is processed in chunks of U vectors per lane.
+//   * Every load and store is a buffer instruction on a per-row buffer resource
+//     whose size is the row's byte length, or 0 for a row that is not live. The
+//     hardware range check then does all masking: lanes past the row end and rows
+//     that are not live read zeros without touching memory, and their stores are
+//     dropped (or, for zero-padded rows, write the +0 that zero inputs produce).
+//     No branch guards a memory instruction, so the compiler's wait counts stay
+//     exact across the software pipeline below.
+//   * Software pipeline: each wave holds two register buffers and issues the loads
+//     of its next chunk (usually its next row) before computing the current one,
+//     so its own memory traffic overlaps its arithmetic.
 //   * Waves stride over rows with a fixed grid (row r, r + W, r + 2W, ...), so the
-//     launch never depends on device data and is graph-safe; the grid is sized so
-//     every wave gets the same number of rows.
+//     launch never depends on device data and is graph-safe; the host sizes the
+//     grid so every wave gets the same number of rows.
 //   * Per-row metadata (permutation slot and probability) for a wave's next 64
 //     rows is gathered with one vector load, one row per lane, and broadcast with
 //     v_readlane when the row is processed: no per-row dependent scalar loads.
@@ -44,12 +52,61 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kMaxU = 4;  // 16-byte vectors per lane per stream per chunk
+#ifndef SWIGLU_MAX_U
+#define SWIGLU_MAX_U 4
+#endif
+constexpr int kMaxU = SWIGLU_MAX_U;  // 16-byte vectors per lane per stream per chunk
+constexpr int kVecBytes = 16;
 constexpr float kNegLog2e = -1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Buffer resources and streaming accesses
+// ---------------------------------------------------------------------------
+// Word 3 of a gfx9-family buffer descriptor for raw (unformatted, stride 0) access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+#ifndef SWIGLU_LOAD_AUX
+#define SWIGLU_LOAD_AUX 2   // cache policy bits of the streaming loads: nt
+#endif
+#ifndef SWIGLU_STORE_AUX
+#define SWIGLU_STORE_AUX 2  // cache policy bits of the streaming stores: nt
+#endif
+
+// Every caller passes wave-uniform values (row addresses and lengths); readfirstlane
+// states that to the compiler, so the descriptor lives in SGPRs and no access needs a
+// per-lane descriptor loop.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kRsrcWord3);
+}
+
+// Resource for the part of a row from byte `off` on: `bytes` is the row's valid
+// length (0 for a row that is not live). Offsets are range-checked relative to the
+// resource, so every access below uses only the lane's VGPR offset.
+__device__ __forceinline__ rsrc_t chunk_rsrc(const uint16_t *row, uint32_t bytes, uint32_t off)
+{
+    return make_rsrc(reinterpret_cast<const char *>(row) + off, bytes > off ? bytes - off : 0u);
+}
+
+__device__ __forceinline__ u32x4 load_vec(rsrc_t r, uint32_t voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, SWIGLU_LOAD_AUX);
+}
+
+__device__ __forceinline__ void store_vec(rsrc_t r, u32x4 v, uint32_t voff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, SWIGLU_STORE_AUX);
+}
 
 // ---------------------------------------------------------------------------
 // Element math
@@ -169,19 +226,20 @@ __device__ __forceinline__ void row_meta(int64_t ri, const RowSchedule &s, const
     }
 }
 
-// ---------------------------------------------------------------------------
-// Forward kernel
-// ---------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
-    const u32x4 *__restrict__ x, const float *__restrict__ probs, u32x4 *__restrict__ y,
-    int rows, int vpr, float L, const int *__restrict__ n_used, const int *__restrict__ perm,
-    int zero_padding)
+// One wave's walk over its rows, in batches of up to 64 rows (one metadata lane
+// each), as a sequence of items (row k of the batch, column chunk c). `Op` loads an
+// item into a register buffer and processes an item from one; the walk issues the
+// loads of item t + 1 before processing item t, alternating two buffers. Loads of
+// items past the end use an empty buffer resource, so they move no data.
+template <class Op>
+__device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, const int *__restrict__ perm,
+                                          const float *__restrict__ probs, int nch)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int W = gridDim.x * kWavesPerBlock;
-    const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+    // the wave index is uniform across the wave; readfirstlane lets the compiler keep
+    // it (and every row address and buffer resource derived from it) in SGPRs
+    const int w = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
     for (int64_t base = w; base < sched.row_end; base += (int64_t)kWave * W) {
         int slot_l;
@@ -189,120 +247,175 @@ __global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
         row_meta(base + (int64_t)lane * W, sched, perm, probs, slot_l, p_l);
         const int64_t left = (sched.row_end - base + W - 1) / W;
         const int nk = left < kWave ? (int)left : kWave;
+        const int T = nk * nch;
 
-        for (int k = 0; k < nk; ++k) {
-            const int64_t r = base + (int64_t)k * W;
+        auto item = [&](int t, int &k, int &c) {
+            k = (nch == 1) ? t : t / nch;
+            c = t - k * nch;
+            if (k >= nk) k = nk - 1;  // past the end: any row of the batch, empty resource
+        };
+        auto prefetch = [&](int t, typename Op::Buf &buf) {
+            int k, c;
+            item(t, k, c);
             const int slot = __builtin_amdgcn_readlane(slot_l, k);
-            u32x4 *__restrict__ yr = y + r * vpr;
-            if (slot >= 0) {
-                const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
-                const u32x4 *__restrict__ gr = x + r * 2 * vpr;
-                const u32x4 *__restrict__ ur = gr + vpr;
-                for (int c0 = 0; c0 < vpr; c0 += kWave * U) {
-                    u32x4 G[U], V[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int v = c0 + u * kWave + lane;
-                        if (v < vpr) {
-                            G[u] = gr[v];
-                            V[u] = ur[v];
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int v = c0 + u * kWave + lane;
-                        if (v < vpr) {
-                            u32x4 o;
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                float y0 = fwd_elem(bf16_lo(G[u][q]), bf16_lo(V[u][q]), p, L);
-                                float y1 = fwd_elem(bf16_hi(G[u][q]), bf16_hi(V[u][q]), p, L);
-                                o[q] = pack_bf16x2(y0, y1);
-                            }
-                            yr[v] = o;
-                        }
-                    }
-                }
-            } else if (zero_padding) {
-                for (int v = lane; v < vpr; v += kWave)
-                    yr[v] = u32x4{0u, 0u, 0u, 0u};
-            }
+            op.load(buf, base + (int64_t)k * W, c, slot >= 0 && t < T);
+        };
+        auto process = [&](int t, const typename Op::Buf &buf) {
+            int k, c;
+            item(t, k, c);
+            const int slot = __builtin_amdgcn_readlane(slot_l, k);
+            const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
+            op.process(buf, base + (int64_t)k * W, c, slot, p);
+        };
+
+        typename Op::Buf A, B;
+        prefetch(0, A);
+        for (int t = 0; t < T; t += 2) {
+            prefetch(t + 1, B);
+            process(t, A);
+            if (t + 1 >= T)
+                break;
+            prefetch(t + 2, A);
+            process(t + 1, B);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Backward kernel
+// Forward
 // ---------------------------------------------------------------------------
 template <int U>
-__global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_kernel(
-    const u32x4 *__restrict__ x, const float *__restrict__ probs, const u32x4 *__restrict__ gy,
-    u32x4 *__restrict__ gx, float *__restrict__ gprobs, int rows, int vpr, float L,
-    const int *__restrict__ n_used, const int *__restrict__ perm, int zero_padding)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int W = gridDim.x * kWavesPerBlock;
-    const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+struct FwdOp {
+    struct Buf {
+        u32x4 g[U], u[U];
+    };
+    const uint16_t *__restrict__ x;
+    uint16_t *__restrict__ y;
+    int inter;
+    float L;
+    int zero_padding;
+    uint32_t voff;  // this lane's byte offset within a chunk
 
-    for (int64_t base = w; base < sched.row_end; base += (int64_t)kWave * W) {
-        int slot_l;
-        float p_l;
-        row_meta(base + (int64_t)lane * W, sched, perm, probs, slot_l, p_l);
-        const int64_t left = (sched.row_end - base + W - 1) / W;
-        const int nk = left < kWave ? (int)left : kWave;
-
-        for (int k = 0; k < nk; ++k) {
-            const int64_t r = base + (int64_t)k * W;
-            const int slot = __builtin_amdgcn_readlane(slot_l, k);
-            u32x4 *__restrict__ dgr = gx + r * 2 * vpr;
-            u32x4 *__restrict__ dur = dgr + vpr;
-            if (slot >= 0) {
-                const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
-                const u32x4 *__restrict__ gr = x + r * 2 * vpr;
-                const u32x4 *__restrict__ ur = gr + vpr;
-                const u32x4 *__restrict__ yr = gy + r * vpr;
-                float acc = 0.0f;
-                for (int c0 = 0; c0 < vpr; c0 += kWave * U) {
-                    u32x4 G[U], V[U], Y[U];
+    __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
+    {
+        const uint16_t *gate = x + r * 2 * inter;
+        const uint32_t n = live ? (uint32_t)inter * 2u : 0u;
+        const uint32_t off = (uint32_t)c * U * kWave * kVecBytes;
+        const rsrc_t rg = chunk_rsrc(gate, n, off), ru = chunk_rsrc(gate + inter, n, off);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int v = c0 + u * kWave + lane;
-                        if (v < vpr) {
-                            G[u] = gr[v];
-                            V[u] = ur[v];
-                            Y[u] = yr[v];
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int v = c0 + u * kWave + lane;
-                        if (v < vpr) {
-                            u32x4 og, ou;
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                float dg0, du0, dg1, du1;
-                                bwd_elem(bf16_lo(G[u][q]), bf16_lo(V[u][q]), bf16_lo(Y[u][q]), p, L,
-                                         dg0, du0, acc);
-                                bwd_elem(bf16_hi(G[u][q]), bf16_hi(V[u][q]), bf16_hi(Y[u][q]), p, L,
-                                         dg1, du1, acc);
-                                og[q] = pack_bf16x2(dg0, dg1);
-                                ou[q] = pack_bf16x2(du0, du1);
-                            }
-                            dgr[v] = og;
-                            dur[v] = ou;
-                        }
-                    }
-                }
-                const float total = wave_sum(acc);
-                if (gprobs && lane == 0)
-                    gprobs[slot] = total;
-            } else if (zero_padding) {
-                for (int v = lane; v < 2 * vpr; v += kWave)
-                    dgr[v] = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int u = 0; u < U; ++u) {
+            b.g[u] = load_vec(rg, voff + u * kWave * kVecBytes);
+            b.u[u] = load_vec(ru, voff + u * kWave * kVecBytes);
         }
     }
+
+    __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p) const
+    {
+        const uint32_t n = (slot >= 0 || zero_padding) ? (uint32_t)inter * 2u : 0u;
+        const rsrc_t ry = chunk_rsrc(y + r * inter, n, (uint32_t)c * U * kWave * kVecBytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float y0 = fwd_elem(bf16_lo(b.g[u][q]), bf16_lo(b.u[u][q]), p, L);
+                float y1 = fwd_elem(bf16_hi(b.g[u][q]), bf16_hi(b.u[u][q]), p, L);
+                o[q] = pack_bf16x2(y0, y1);
+            }
+            store_vec(ry, o, voff + u * kWave * kVecBytes);
+        }
+    }
+};
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ probs, uint16_t *__restrict__ y,
+    int rows, int inter, float L, const int *__restrict__ n_used, const int *__restrict__ perm,
+    int zero_padding)
+{
+    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+    const int vpr = inter / 8;
+    const int nch = (vpr + U * kWave - 1) / (U * kWave);
+    FwdOp<U> op{x, y, inter, L, zero_padding, (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes};
+    walk_rows(op, sched, perm, probs, nch);
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+template <int U>
+struct BwdOp {
+    struct Buf {
+        u32x4 g[U], u[U], d[U];
+    };
+    const uint16_t *__restrict__ x;
+    const uint16_t *__restrict__ gy;
+    uint16_t *__restrict__ gx;
+    float *__restrict__ gprobs;
+    int inter;
+    int nch;
+    float L;
+    int zero_padding;
+    uint32_t voff;
+    float acc;  // this lane's partial of the current row's probability gradient
+
+    __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
+    {
+        const uint16_t *gate = x + r * 2 * inter;
+        const uint32_t n = live ? (uint32_t)inter * 2u : 0u;
+        const uint32_t off = (uint32_t)c * U * kWave * kVecBytes;
+        const rsrc_t rg = chunk_rsrc(gate, n, off), ru = chunk_rsrc(gate + inter, n, off);
+        const rsrc_t rd = chunk_rsrc(gy + r * inter, n, off);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            b.g[u] = load_vec(rg, voff + u * kWave * kVecBytes);
+            b.u[u] = load_vec(ru, voff + u * kWave * kVecBytes);
+            b.d[u] = load_vec(rd, voff + u * kWave * kVecBytes);
+        }
+    }
+
+    __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p)
+    {
+        const uint32_t n = (slot >= 0 || zero_padding) ? (uint32_t)inter * 2u : 0u;
+        uint16_t *dgate = gx + r * 2 * inter;
+        const uint32_t off = (uint32_t)c * U * kWave * kVecBytes;
+        const rsrc_t rdg = chunk_rsrc(dgate, n, off), rdu = chunk_rsrc(dgate + inter, n, off);
+        if (c == 0)
+            acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 og, ou;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float dg0, du0, dg1, du1;
+                bwd_elem(bf16_lo(b.g[u][q]), bf16_lo(b.u[u][q]), bf16_lo(b.d[u][q]), p, L, dg0, du0, acc);
+                bwd_elem(bf16_hi(b.g[u][q]), bf16_hi(b.u[u][q]), bf16_hi(b.d[u][q]), p, L, dg1, du1, acc);
+                og[q] = pack_bf16x2(dg0, dg1);
+                ou[q] = pack_bf16x2(du0, du1);
+            }
+            store_vec(rdg, og, voff + u * kWave * kVecBytes);
+            store_vec(rdu, ou, voff + u * kWave * kVecBytes);
+        }
+        if (c == nch - 1 && slot >= 0 && gprobs) {
+            const float total = wave_sum(acc);
+            if ((threadIdx.x & (kWave - 1)) == 0)
+                gprobs[slot] = total;
+        }
+    }
+};
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ probs, const uint16_t *__restrict__ gy,
+    uint16_t *__restrict__ gx, float *__restrict__ gprobs, int rows, int inter, float L,
+    const int *__restrict__ n_used, const int *__restrict__ perm, int zero_padding)
+{
+    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+    const int vpr = inter / 8;
+    const int nch = (vpr + U * kWave - 1) / (U * kWave);
+    BwdOp<U> op{x, gy, gx, gprobs, inter, nch, L, zero_padding,
+                (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes, 0.0f};
+    walk_rows(op, sched, perm, probs, nch);
 }
 
 // ---------------------------------------------------------------------------
@@ -316,8 +429,8 @@ struct DeviceLaunchInfo {
     std::once_flag once;
     hipError_t err = hipSuccess;
     int cus = 0;
-    int fwd_blocks_per_cu[kMaxU + 1] = {};
-    int bwd_blocks_per_cu[kMaxU + 1] = {};
+    int fwd_blocks_per_cu[5] = {};  // indexed by U (1..4)
+    int bwd_blocks_per_cu[5] = {};
 };
 DeviceLaunchInfo g_devices[kMaxDevices];
 
@@ -369,8 +482,20 @@ int pick_u(int64_t vpr)
 
 // Workgroups so that the resident waves divide the rows evenly: with R rows and at
 // most M resident waves, rounds = ceil(R / M) and W = ceil(R / rounds) waves.
-int balanced_workgroups(int64_t rows, int cus, int blocks_per_cu)
+// Workgroups per CU of the default launch: one (four waves, one per SIMD). Each wave
+// keeps its next chunk's loads in flight while it computes the current one, and on
+// MI355X's HBM3E more resident waves only add concurrent request streams: measured
+// throughput at the 1.1 GB shape falls from ~6.0 TB/s at one workgroup per CU to
+// ~5.6 TB/s at two to four. Capped by the kernel's occupancy limit.
+#ifndef SWIGLU_BLOCKS_PER_CU
+#define SWIGLU_BLOCKS_PER_CU 1
+#endif
+constexpr int kLaunchBlocksPerCU = SWIGLU_BLOCKS_PER_CU;
+
+int balanced_workgroups(int64_t rows, int cus, int resident_blocks_per_cu)
 {
+    int blocks_per_cu = resident_blocks_per_cu < kLaunchBlocksPerCU ? resident_blocks_per_cu
+                                                                     : kLaunchBlocksPerCU;
     if (blocks_per_cu < 1)
         blocks_per_cu = 1;
     const int64_t max_waves = (int64_t)cus * blocks_per_cu * kWavesPerBlock;
@@ -426,21 +551,19 @@ swiglu_status_t fail_hip(hipError_t e)
 
 template <int U>
 void launch_fwd(int blocks, hipStream_t stream, const uint16_t *x, const float *probs, uint16_t *y,
-                int rows, int vpr, float limit, const int32_t *n_used, const int32_t *perm, int zp)
+                int rows, int inter, float limit, const int32_t *n_used, const int32_t *perm, int zp)
 {
-    hipLaunchKernelGGL(swiglu_probs_fwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream,
-                       reinterpret_cast<const u32x4 *>(x), probs, reinterpret_cast<u32x4 *>(y), rows,
-                       vpr, limit, n_used, perm, zp);
+    hipLaunchKernelGGL(swiglu_probs_fwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream, x, probs, y,
+                       rows, inter, limit, n_used, perm, zp);
 }
 
 template <int U>
 void launch_bwd(int blocks, hipStream_t stream, const uint16_t *x, const float *probs,
-                const uint16_t *gy, uint16_t *gx, float *gp, int rows, int vpr, float limit,
+                const uint16_t *gy, uint16_t *gx, float *gp, int rows, int inter, float limit,
                 const int32_t *n_used, const int32_t *perm, int zp)
 {
-    hipLaunchKernelGGL(swiglu_probs_bwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream,
-                       reinterpret_cast<const u32x4 *>(x), probs, reinterpret_cast<const u32x4 *>(gy),
-                       reinterpret_cast<u32x4 *>(gx), gp, rows, vpr, limit, n_used, perm, zp);
+    hipLaunchKernelGGL(swiglu_probs_bwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream, x, probs, gy,
+                       gx, gp, rows, inter, limit, n_used, perm, zp);
 }
 
 }  // namespace
@@ -483,10 +606,10 @@ swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint1
                                           : balanced_workgroups(rows, info->cus, info->fwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
     switch (U) {
-    case 1: launch_fwd<1>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
-    case 2: launch_fwd<2>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
-    case 3: launch_fwd<3>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
-    default: launch_fwd<4>(blocks, stream, x, probs, y, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    case 1: launch_fwd<1>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    case 2: launch_fwd<2>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    case 3: launch_fwd<3>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    default: launch_fwd<4>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
     }
     e = hipGetLastError();
     if (e != hipSuccess)
@@ -531,10 +654,10 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
                                           : balanced_workgroups(rows, info->cus, info->bwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
     switch (U) {
-    case 1: launch_bwd<1>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
-    case 2: launch_bwd<2>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
-    case 3: launch_bwd<3>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
-    default: launch_bwd<4>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, vpr, limit, n_used, permutation_map, zp); break;
+    case 1: launch_bwd<1>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    case 2: launch_bwd<2>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    case 3: launch_bwd<3>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    default: launch_bwd<4>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
     }
     e = hipGetLastError();
     if (e != hipSuccess)

@@ -14,6 +14,9 @@ Printed JSON line (stdout):
                its average duration, against the 8 TB/s MI355X HBM peak; traffic =
                HBM bytes per launch from the committed rocprofv3 counter summary when
                it was taken on the current kernel source, else null
+  cold         the same kernels timed one launch at a time after a read of an unrelated
+               1 GiB buffer (evicts the 256 MB Infinity Cache without leaving dirty
+               lines), so no input can come from the previous launch's cache state
   hbm_probe    plain streaming kernels (1:1 copy, 2:1 and 3:2 read:write) moving the
                same bytes as fwd / bwd: the practical ceiling on this device
   cpu_baseline the CPU oracle (test infrastructure, untuned) on the same inputs,
@@ -81,6 +84,8 @@ def main() -> int:
                     choices=["tiny", "mid", "headline", "padded", "edge"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="launches of each kernel timed after a cache-evicting read (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--fwd-workgroups", type=int, default=0)
@@ -153,6 +158,31 @@ def main() -> int:
     value = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e6)
     log(f"fwd {f_avg * 1e3:.1f} us ({f_gbs:.0f} GB/s), bwd {b_avg * 1e3:.1f} us ({b_gbs:.0f} GB/s), "
         f"step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s)")
+
+    cold = None
+    if args.cold_reps > 0:
+        log(f"cold: {args.cold_reps} launches of each kernel after a 1 GiB read")
+        evict = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        cf, cb = [], []
+        for _ in range(args.cold_reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            evict.sum(dtype=torch.int64)
+            ev[0].record()
+            swiglu_probs_fwd(x, probs, y, L, num_workgroups=args.fwd_workgroups, **kw)
+            ev[1].record()
+            evict.sum(dtype=torch.int64)
+            ev[2].record()
+            swiglu_probs_bwd(x, probs, gy, gx, gp, L, num_workgroups=args.bwd_workgroups, **kw)
+            ev[3].record()
+            torch.cuda.synchronize()
+            cf.append(ev[0].elapsed_time(ev[1]))
+            cb.append(ev[2].elapsed_time(ev[3]))
+        del evict
+        cfm, cbm = float(np.median(cf)), float(np.median(cb))
+        cold = {"fwd_us": round(cfm * 1e3, 2), "fwd_GB/s": round(fwd_bytes / (cfm * 1e6), 1),
+                "bwd_us": round(cbm * 1e3, 2), "bwd_GB/s": round(bwd_bytes / (cbm * 1e6), 1),
+                "reps": args.cold_reps, "statistic": "median"}
+        log(f"cold: fwd {cold['fwd_GB/s']} GB/s, bwd {cold['bwd_GB/s']} GB/s")
 
     probe = None
     if not args.no_probe:
@@ -232,6 +262,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "swiglu_probs_bwd_kernel",
                      "achieved": round(b_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(b_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "cold": cold,
         "hbm_probe": probe,
         "cpu_baseline": cpu,
         "context": "pages' only figure: inductor-compiled autograd backward on GB200, ~0.7 ms per "

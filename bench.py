@@ -221,7 +221,7 @@ def main() -> int:
         okw = dict(n_used=inp["n_used"], permutation_map=inp["permutation_map"],
                    zero_padding=inp["zero_padding"], threads=threads)
         reps, spent = 0, 0.0
-        while reps < 1 or (spent < args.cpu_seconds and reps < 20):
+        while reps < 1 or (spent < args.cpu_seconds and reps < 200):
             t = time.perf_counter()
             orc.fwd(inp["x"], inp["probs"], L, **okw)
             orc.bwd(inp["x"], inp["probs"], inp["grad_y"], L, **okw)

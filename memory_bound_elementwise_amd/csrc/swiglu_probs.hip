@@ -254,11 +254,14 @@ __device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, cons
             c = t - k * nch;
             if (k >= nk) k = nk - 1;  // past the end: any row of the batch, empty resource
         };
+        // Without a map a row is live iff it is below the live bound, so its loads do
+        // not wait for the metadata gather; with a map the slot decides.
         auto prefetch = [&](int t, typename Op::Buf &buf) {
             int k, c;
             item(t, k, c);
-            const int slot = __builtin_amdgcn_readlane(slot_l, k);
-            op.load(buf, base + (int64_t)k * W, c, slot >= 0 && t < T);
+            const int64_t r = base + (int64_t)k * W;
+            const bool live = perm ? __builtin_amdgcn_readlane(slot_l, k) >= 0 : r < sched.live;
+            op.load(buf, r, c, live && t < T);
         };
         auto process = [&](int t, const typename Op::Buf &buf) {
             int k, c;

@@ -20,7 +20,7 @@ LIB_DIR = os.path.join(PKG, "_lib")
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
-HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", f"-I{CSRC}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-result"]
 

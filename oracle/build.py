@@ -13,6 +13,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "swiglu_oracle.c")
 LIB_PATH = os.path.join(HERE, "liboracle_swiglu.so")
+MOE_SOURCE = os.path.join(HERE, "moe_oracle.c")
+MOE_LIB_PATH = os.path.join(HERE, "liboracle_moe.so")
 
 # No fast-math and no FMA contraction: every fp32 operation is rounded as written.
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
@@ -44,6 +46,8 @@ def compile_oracle(source: str = SOURCE, out: str = LIB_PATH, extra_flags=()) ->
 
 
 def build() -> str:
+    """Compile both oracle libraries; returns the SwiGLU one's path."""
+    compile_oracle(MOE_SOURCE, MOE_LIB_PATH)
     return compile_oracle()
 
 

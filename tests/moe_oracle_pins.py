@@ -1,0 +1,240 @@
+"""Pins of the MoE-ops oracle (``oracle/moe.py``) against values fixed independently.
+
+Each ``pin_*`` takes a ``MoeOracle`` and raises ``AssertionError`` on disagreement.
+
+* fp16 conversions     -> pin_f16_conversions (numpy's float16 casts, every pattern)
+* residual add         -> pin_residual_add (torch CPU: residual + (expert + shared) in
+                          the same dtype, i.e. the two unfused adds, bitwise)
+* router weight fwd    -> pin_router_weight_fwd (torch (x.float() * p).to(dtype), bitwise)
+* router weight bwd    -> pin_router_weight_bwd (torch fp32 autograd of that expression:
+                          grad_x bitwise, grad_probs on the row-scale criterion; fp64 sums)
+* squared ReLU         -> pin_squared_relu_no_clamp (torch bf16 relu(x)**2, then * p,
+                          bitwise), pin_squared_relu_clamp (torch fp64 reference within
+                          1 ulp; large scale reduces to the unclamped fp32 square),
+                          pin_squared_relu_rows (n_used / map / padding rules)
+* unpermute            -> pin_unpermute (numpy float32 running sums in expert order;
+                          single-contribution tokens copy the row exactly; bounds)
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from bf16cmp import assert_within_ulp, bf16_bits_to_f32, grad_probs_violations
+
+DT_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _np_to_torch(a: np.ndarray, dt: str) -> torch.Tensor:
+    if dt == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(DT_TORCH[dt])
+
+
+def _torch_to_np(t: torch.Tensor, dt: str) -> np.ndarray:
+    if dt == "f32":
+        return t.to(torch.float32).numpy()
+    return t.to(DT_TORCH[dt]).view(torch.int16).numpy().view(np.uint16)
+
+
+def _draw(shape, dt, rng, scale=1.0, specials=True):
+    v = (rng.standard_normal(shape) * scale).astype(np.float32)
+    if specials:
+        flat = v.reshape(-1)
+        k = max(1, flat.size // 200)
+        idx = rng.choice(flat.size, size=k * 6, replace=False)
+        flat[idx[:k]] = np.inf
+        flat[idx[k:2 * k]] = -np.inf
+        flat[idx[2 * k:3 * k]] = np.nan
+        flat[idx[3 * k:4 * k]] = 0.0
+        flat[idx[4 * k:5 * k]] = -0.0
+        flat[idx[5 * k:]] = 1e-41 if dt != "f16" else 3e-6
+    return _torch_to_np(torch.from_numpy(v), dt)
+
+
+def _same_bits(a: np.ndarray, b: np.ndarray, dt: str) -> np.ndarray:
+    if dt == "f32":
+        an, bn = np.isnan(a), np.isnan(b)
+        return (a.view(np.uint32) == b.view(np.uint32)) | (an & bn)
+    aexp = (a & 0x7F80) == 0x7F80 if dt == "bf16" else (a & 0x7C00) == 0x7C00
+    bexp = (b & 0x7F80) == 0x7F80 if dt == "bf16" else (b & 0x7C00) == 0x7C00
+    mant = 0x7F if dt == "bf16" else 0x3FF
+    an = aexp & ((a & mant) != 0)
+    bn = bexp & ((b & mant) != 0)
+    return (a == b) | (an & bn)
+
+
+def pin_f16_conversions(orc):
+    allp = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.f32_from_f16(allp)
+    want = allp.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32)), "fp16 -> fp32"
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 2**32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # fp32 values on and around fp16 rounding boundaries, incl. the subnormal range
+    halves = (allp.view(np.float16).astype(np.float32))
+    fin = np.isfinite(halves)
+    mids = ((halves[fin][:-1].astype(np.float64) + halves[fin][1:]) / 2).astype(np.float32)
+    f = np.concatenate([bits.view(np.float32), mids, np.nextafter(mids, np.inf),
+                        np.nextafter(mids, -np.inf), np.float32([65504, 65519.99, 65520, 65536, 1e9])])
+    got = orc.f16_from_f32(f)
+    with np.errstate(over="ignore"):
+        want = f.astype(np.float16).view(np.uint16)
+    ok = _same_bits(got, want, "f16")
+    assert ok.all(), f"fp32 -> fp16 differs at {np.flatnonzero(~ok)[:5]} ({f[~ok][:5]})"
+
+
+def pin_residual_add(orc):
+    rng = np.random.default_rng(1)
+    for dt in ("bf16", "f16", "f32"):
+        n = 1 << 18
+        e = _draw(n, dt, rng, 4.0)
+        s = _draw(n, dt, rng, 4.0)
+        r = _draw(n, dt, rng, 100.0)
+        got = orc.residual_add(e, s, r, dt)
+        te, ts, tr = (_np_to_torch(v, dt) for v in (e, s, r))
+        want = _torch_to_np(tr + (te + ts), dt)
+        ok = _same_bits(got, want, dt)
+        assert ok.all(), f"residual add {dt}: {int((~ok).sum())} mismatches"
+        # the inner sum is rounded to the dtype before the residual add: for 16-bit
+        # types a single fp32 sum of all three differs somewhere
+        if dt != "f32":
+            one = _torch_to_np((tr.float() + (te.float() + ts.float())).to(DT_TORCH[dt]), dt)
+            assert not _same_bits(got, one, dt).all(), "inner rounding not observable"
+
+
+def pin_router_weight_fwd(orc):
+    rng = np.random.default_rng(2)
+    for x_dt in ("bf16", "f16", "f32"):
+        for out_dt in sorted({x_dt, "f32"}):
+            x = _draw((64, 96), x_dt, rng, 3.0)
+            p = rng.uniform(0, 1, 64).astype(np.float32)
+            p[3] = 0.0
+            got = orc.router_weight_fwd(x, x_dt, p, out_dt)
+            want = _torch_to_np((_np_to_torch(x, x_dt).float() * torch.from_numpy(p)[:, None])
+                                .to(DT_TORCH[out_dt]), out_dt)
+            assert _same_bits(got, want, out_dt).all(), f"router fwd {x_dt}->{out_dt}"
+
+
+def pin_router_weight_bwd(orc):
+    rng = np.random.default_rng(3)
+    for x_dt in ("bf16", "f16", "f32"):
+        for out_dt in sorted({x_dt, "f32"}):
+            x = _draw((48, 160), x_dt, rng, 3.0, specials=False)
+            g = _draw((48, 160), out_dt, rng, 1.0, specials=False)
+            p = rng.uniform(0, 1, 48).astype(np.float32)
+            o = orc.router_weight_bwd(g, out_dt, x, x_dt, p)
+            tx = _np_to_torch(x, x_dt).float().requires_grad_(True)
+            tp = torch.from_numpy(p)[:, None].clone().requires_grad_(True)
+            y = (tx * tp).to(DT_TORCH[out_dt])
+            y.backward(_np_to_torch(g, out_dt))
+            assert _same_bits(o["grad_x"], _torch_to_np(tx.grad, x_dt), x_dt).all(), \
+                f"router grad_x {x_dt}/{out_dt}"
+            exact = (_np_to_torch(g, out_dt).double() * _np_to_torch(x, x_dt).double()).sum(-1).numpy()
+            bad = grad_probs_violations(o["grad_probs"], exact, o["row_scale"])
+            assert bad.size == 0, f"router grad_probs {x_dt}/{out_dt}"
+            bad = grad_probs_violations(tp.grad.reshape(-1).numpy(), exact, o["row_scale"])
+            assert bad.size == 0, "torch's own fp32 sum must meet the same bar"
+            assert np.allclose(o["grad_probs_f64"], exact, rtol=0, atol=1e-6 * o["row_scale"].max())
+    # without grad_probs nothing reads x
+    o = orc.router_weight_bwd(_draw((4, 8), "bf16", rng), "bf16", None, "bf16",
+                              np.ones(4, np.float32), want_grad_probs=False)
+    assert o["grad_probs"] is None
+
+
+def pin_squared_relu_no_clamp(orc):
+    rng = np.random.default_rng(4)
+    x = _draw((96, 256), "bf16", rng, 8.0)
+    p = rng.uniform(0, 1, 96).astype(np.float32)
+    got = orc.squared_relu_probs(x, p)
+    tx = _np_to_torch(x, "bf16")
+    sq = torch.relu(tx) * torch.relu(tx)          # a bf16 tensor op: fp32 product, one rounding
+    want = _torch_to_np(sq.float() * torch.from_numpy(p)[:, None], "bf16")
+    assert _same_bits(got, want, "bf16").all(), "squared relu without clamp"
+    # the square really is rounded to bf16 first: a single fp32 chain differs somewhere
+    one = _torch_to_np(torch.relu(tx.float()) ** 2 * torch.from_numpy(p)[:, None], "bf16")
+    assert not (got == one).all()
+
+
+def pin_squared_relu_clamp(orc):
+    rng = np.random.default_rng(5)
+    x = _draw((64, 256), "bf16", rng, 8.0, specials=False)
+    p = rng.uniform(0.01, 1, 64).astype(np.float32)
+    for s in (0.5, 3.0, 20.0):
+        got = orc.squared_relu_probs(x, p, clamp_scale=s)
+        xd = torch.from_numpy(bf16_bits_to_f32(x).astype(np.float64))
+        want = torch.relu(s * torch.tanh(xd / s)) ** 2 * torch.from_numpy(p.astype(np.float64))[:, None]
+        assert_within_ulp(got, _torch_to_np(want.float(), "bf16"), 1, f"soft clamp s={s}")
+        assert bf16_bits_to_f32(got).max() <= s * s * 1.0001, "soft clamp bound"
+    # a large scale reduces the soft clamp to the identity: relu(x)^2 * p in fp32
+    got = orc.squared_relu_probs(x, p, clamp_scale=1e6)
+    want = torch.relu(torch.from_numpy(bf16_bits_to_f32(x))) ** 2 * torch.from_numpy(p)[:, None]
+    assert_within_ulp(got, _torch_to_np(want, "bf16"), 1, "s -> inf")
+
+
+def pin_squared_relu_rows(orc):
+    rng = np.random.default_rng(6)
+    x = _draw((40, 64), "bf16", rng, 3.0, specials=False)
+    p = rng.uniform(0, 1, 40).astype(np.float32)
+    full = orc.squared_relu_probs(x, p, clamp_scale=2.0)
+    perm = rng.permutation(40).astype(np.int32)
+    assert np.array_equal(orc.squared_relu_probs(x, p, clamp_scale=2.0, permutation_map=perm),
+                          orc.squared_relu_probs(x, p[perm], clamp_scale=2.0))
+    for k in (0, 13, 40):
+        for zp in (False, True):
+            y = orc.squared_relu_probs(x, p, clamp_scale=2.0, n_used=k, zero_padding=zp)
+            assert np.array_equal(y[:k], full[:k])
+            assert np.all(y[k:] == (0 if zp else 0xFFFF))
+    pm = np.arange(40, dtype=np.int32)
+    pm[[2, 9]] = [-1, 40]
+    y = orc.squared_relu_probs(x, p, clamp_scale=2.0, permutation_map=pm, zero_padding=True)
+    assert np.all(y[[2, 9]] == 0) and np.array_equal(np.delete(y, [2, 9], 0), np.delete(full, [2, 9], 0))
+
+
+def pin_unpermute(orc):
+    rng = np.random.default_rng(7)
+    tokens, E, hidden, erows = 50, 6, 48, 120
+    eo = _draw((erows, hidden), "bf16", rng, 2.0, specials=False)
+    im = rng.integers(-1, erows, size=(tokens, E)).astype(np.int32)
+    im[rng.random((tokens, E)) < 0.4] = -1
+    im[0] = -1                       # a token with no local contribution
+    im[1, 2] = erows + 5             # out of range: skipped
+    for out_dt in ("f32", "bf16"):
+        got = orc.unpermute(eo, im, out_dt)
+        ef = bf16_bits_to_f32(eo)
+        acc = np.zeros((tokens, hidden), np.float32)
+        for e in range(E):           # running fp32 sums in increasing expert id
+            rows = im[:, e]
+            ok = (rows >= 0) & (rows < erows)
+            acc[ok] = acc[ok] + ef[rows[ok]]
+        want = acc if out_dt == "f32" else _torch_to_np(torch.from_numpy(acc), "bf16")
+        assert _same_bits(got, want, out_dt).all(), f"unpermute {out_dt}"
+    # one contribution per token copies the row exactly
+    im1 = np.full((tokens, E), -1, np.int32)
+    im1[np.arange(tokens), rng.integers(0, E, tokens)] = rng.integers(0, erows, tokens)
+    got = orc.unpermute(eo, im1, "bf16")
+    assert np.array_equal(got, eo[im1.max(axis=1)])
+    # tokens at or past valid_tokens are untouched
+    got = orc.unpermute(eo, im, "bf16", valid_tokens=17)
+    assert np.all(got[17:] == 0xFFFF) and np.array_equal(got[:17], orc.unpermute(eo, im, "bf16")[:17])
+    assert np.all(orc.unpermute(eo, im, "bf16", valid_tokens=-3) == 0xFFFF)
+    # the order is increasing expert id: contributions 2^24, 1, -2^24 sum to 0 in that
+    # order (2^24 + 1 rounds to 2^24 in fp32) and to 1 in the reverse order
+    big = np.zeros((3, hidden), np.uint16)
+    big[0] = 0x4B80                  # 2^24
+    big[1] = 0x3F80                  # 1
+    big[2] = 0xCB80                  # -2^24
+    order = orc.unpermute(big, np.array([[0, 1, 2], [2, 1, 0]], np.int32), "f32")
+    assert np.all(order[0] == 0.0) and np.all(order[1] == 1.0), "expert order of the fp32 sum"
+    # order matters only through rounding: reversing the experts stays within fp32 error
+    rev = orc.unpermute(eo, im[:, ::-1].copy(), "f32")
+    fwd = orc.unpermute(eo, im, "f32")
+    assert np.allclose(rev, fwd, rtol=0, atol=E * 2 * math.ldexp(1, -24) * np.abs(fwd).max() + 1e-30)
+
+
+ALL_PINS = [pin_f16_conversions, pin_residual_add, pin_router_weight_fwd, pin_router_weight_bwd,
+            pin_squared_relu_no_clamp, pin_squared_relu_clamp, pin_squared_relu_rows, pin_unpermute]

@@ -1,0 +1,63 @@
+"""Plant one mistake at a time in a copy of the MoE-ops oracle source (on the CPU)
+and require that some pin of ``moe_oracle_pins.py`` fails for each."""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+from oracle import build as obuild
+from oracle.moe import MoeOracle
+from moe_oracle_pins import ALL_PINS
+
+MUTANTS = [
+    ("residual_no_inner_rounding",
+     "float t = round_to(load_elem(expert, i, dt) + load_elem(shared, i, dt), dt);",
+     "float t = load_elem(expert, i, dt) + load_elem(shared, i, dt);"),
+    ("residual_wrong_operand",
+     "float t = round_to(load_elem(expert, i, dt) + load_elem(shared, i, dt), dt);",
+     "float t = round_to(load_elem(expert, i, dt) + load_elem(residual, i, dt), dt);"),
+    ("f16_ties_away", "    float r = nearbyintf(n);\n    if (r == 2048.0f)", "    float r = roundf(n);\n    if (r == 2048.0f)"),
+    ("f16_subnormal_truncated", "float r = nearbyintf(n);   /* default", "float r = truncf(n);   /* default"),
+    ("router_fwd_wrong_prob", "load_elem(x, t * hidden + h, x_dt) * probs[t]);", "load_elem(x, t * hidden + h, x_dt) * probs[0]);"),
+    ("router_grad_x_no_prob", "store_elem(grad_x, t * hidden + h, x_dt, g * probs[t]);", "store_elem(grad_x, t * hidden + h, x_dt, g);"),
+    ("router_grad_probs_times_p", "float term = g * load_elem(x, t * hidden + h, x_dt);",
+     "float term = g * load_elem(x, t * hidden + h, x_dt) * probs[t];"),
+    ("sqrelu_square_not_rounded", "float sq = bf16_to_f32(f32_to_bf16(a * a));", "float sq = a * a;"),
+    ("sqrelu_scale_inverted", "tanhf(v / clamp_scale)", "tanhf(v * clamp_scale)"),
+    ("sqrelu_no_relu", "float a = c < 0.0f ? 0.0f : c;", "float a = c;"),
+    ("sqrelu_map_not_gathered", "const float p = probs[slot];", "const float p = probs[r];"),
+    ("unpermute_reversed", "for (int64_t e = 0; e < num_local_experts; ++e) {",
+     "for (int64_t e = num_local_experts - 1; e >= 0; --e) {"),
+    ("unpermute_bound_off_by_one", "for (int64_t t = 0; t < bound; ++t)", "for (int64_t t = 0; t < bound + (bound < tokens); ++t)"),
+]
+
+
+def _failed(orc):
+    out = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError):
+            out.append(pin.__name__)
+    return out
+
+
+@pytest.fixture(scope="module")
+def source_text():
+    with open(obuild.MOE_SOURCE) as fh:
+        return fh.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(source_text, name, old, new):
+    assert source_text.count(old) == 1, f"mutation site for {name} not unique/found"
+    tmp = tempfile.mkdtemp(prefix="moe_oracle_mutant_")
+    try:
+        src = os.path.join(tmp, "mutant.c")
+        with open(src, "w") as fh:
+            fh.write(source_text.replace(old, new))
+        lib = obuild.compile_oracle(src, os.path.join(tmp, "libmutant.so"))
+        assert _failed(MoeOracle(lib)), f"no pin caught the planted mistake {name}"
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)

@@ -1,7 +1,8 @@
 """Build the HIP libraries of this package for gfx950, in-tree.
 
 ``libswiglu_probs.so`` holds the activation kernels and their C ABI
-(``include/swiglu_probs.h``); ``libhbm_probe.so`` holds plain streaming kernels
+(``include/swiglu_probs.h``); ``libmoe_elementwise.so`` the MoE elementwise
+operations next to it (``include/moe_elementwise.h``); ``libhbm_probe.so`` holds plain streaming kernels
 that measure the practical HBM ceiling and calibrate the hardware byte counters
 (``include/hbm_probe.h``). Both are written to ``memory_bound_elementwise_amd/_lib``.
 """
@@ -26,6 +27,7 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", f
 
 LIBS = {
     "swiglu_probs": ["swiglu_probs.hip"],
+    "moe_elementwise": ["moe_elementwise.hip"],
     "hbm_probe": ["hbm_probe.hip"],
 }
 

@@ -222,6 +222,30 @@ __device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, cons
     }
 }
 
+// The same two-buffer pipeline over `n_blocks` equal blocks of a flat array, with no
+// per-row metadata: block b goes to wave b mod W. Op::load(buf, b, live) and
+// Op::process(buf, b).
+template <class Op>
+__device__ __forceinline__ void walk_blocks(Op &op, int64_t n_blocks)
+{
+    const int64_t W = (int64_t)gridDim.x * kWavesPerBlock;
+    const int64_t w = wave_id();
+    if (w >= n_blocks)
+        return;
+    const int64_t T = (n_blocks - w + W - 1) / W;  // blocks of this wave
+    auto block = [&](int64_t t) { return w + (t < T ? t : T - 1) * W; };
+    typename Op::Buf A, B;
+    op.load(A, block(0), true);
+    for (int64_t t = 0; t < T; t += 2) {
+        op.load(B, block(t + 1), t + 1 < T);
+        op.process(A, block(t));
+        if (t + 1 >= T)
+            break;
+        op.load(A, block(t + 2), t + 2 < T);
+        op.process(B, block(t + 1));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: launch sizing
 // ---------------------------------------------------------------------------

@@ -1,0 +1,840 @@
+// MoE elementwise operations next to the routed-expert activation, for AMD Instinct
+// MI355X (gfx950). C ABI declared in moe_elementwise.h.
+//
+//   residual add   Megatron-Core "core.fusions.fused_moe_residual_add" page
+//   router weight  NeMo AutoModel "moe/optimized_ops" page (_RouterWeightMulFunction)
+//   squared ReLU   Megatron-Core "core.inference.moe.batch_invariant" page
+//                  (_squared_relu_with_probs_kernel, squared_relu_with_probs)
+//   unpermute      same page (_unpermute_tokens_in_expert_order_kernel)
+//
+// All four are HBM-bound streams built on cdna4_stream.h: 128-bit buffer accesses
+// on per-row (or per-block) resources whose hardware range check masks ragged ends
+// and rows that are not live, nontemporal hints, one workgroup per CU, and the
+// two-buffer software pipeline per wave. Values are handled in groups of eight
+// elements per lane ("octs": one 16-byte access for 16-bit types, two for fp32).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "cdna4_stream.h"
+#include "moe_elementwise.h"
+
+namespace {
+
+using namespace cdna4;
+
+enum : int { DT_BF16 = 0, DT_F16 = 1, DT_F32 = 2 };
+
+template <int DT>
+constexpr int kElemBytes = DT == DT_F32 ? 4 : 2;
+template <int DT>
+constexpr int kOctBytes = 8 * kElemBytes<DT>;
+
+struct Oct {
+    u32x4 v[2];  // v[1] used only for fp32
+};
+
+template <int DT>
+__device__ __forceinline__ Oct load_oct(rsrc_t r, uint32_t off)
+{
+    Oct o;
+    o.v[0] = load_vec(r, off);
+    if constexpr (DT == DT_F32)
+        o.v[1] = load_vec(r, off + kVecBytes);
+    return o;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_oct(rsrc_t r, const Oct &o, uint32_t off)
+{
+    store_vec(r, o.v[0], off);
+    if constexpr (DT == DT_F32)
+        store_vec(r, o.v[1], off + kVecBytes);
+}
+
+template <int DT>
+__device__ __forceinline__ void widen(const Oct &o, float (&f)[8])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == DT_BF16) {
+            f[2 * q] = bf16_lo(o.v[0][q]);
+            f[2 * q + 1] = bf16_hi(o.v[0][q]);
+        } else if constexpr (DT == DT_F16) {
+            const f32x2 t = unpack_f16x2(o.v[0][q]);
+            f[2 * q] = t.x;
+            f[2 * q + 1] = t.y;
+        } else {
+            f[q] = __uint_as_float(o.v[0][q]);
+            f[4 + q] = __uint_as_float(o.v[1][q]);
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ Oct narrow(const float (&f)[8])
+{
+    Oct o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == DT_BF16) {
+            o.v[0][q] = pack_bf16x2(f[2 * q], f[2 * q + 1]);
+        } else if constexpr (DT == DT_F16) {
+            o.v[0][q] = pack_f16x2(f[2 * q], f[2 * q + 1]);
+        } else {
+            o.v[0][q] = __float_as_uint(f[q]);
+            o.v[1][q] = __float_as_uint(f[4 + q]);
+        }
+    }
+    return o;
+}
+
+// Rounds eight fp32 values to DT and back (the activation-dtype rounding of a sum).
+template <int DT>
+__device__ __forceinline__ void round_to(float (&f)[8])
+{
+    if constexpr (DT != DT_F32)
+        widen<DT>(narrow<DT>(f), f);
+}
+
+// ---------------------------------------------------------------------------
+// Fused MoE residual add: out = residual + round_to_dtype(expert + shared)
+// ---------------------------------------------------------------------------
+template <int DT, int U>
+struct ResidualAddOp {
+    static constexpr uint32_t kBlockBytes = U * kWave * kOctBytes<DT>;
+    struct Buf {
+        Oct e[U], s[U], r[U];
+    };
+    const char *e, *s, *r;
+    char *out;
+    int64_t full_bytes;  // bytes of the whole octs of each tensor
+    uint32_t voff;       // this lane's offset within a block
+
+    __device__ __forceinline__ uint32_t valid(int64_t b) const
+    {
+        const int64_t left = full_bytes - b * kBlockBytes;
+        return left <= 0 ? 0u : (left < kBlockBytes ? (uint32_t)left : kBlockBytes);
+    }
+
+    __device__ __forceinline__ void load(Buf &buf, int64_t b, bool live) const
+    {
+        const int64_t off = b * kBlockBytes;
+        const uint32_t n = live ? valid(b) : 0u;
+        const rsrc_t re = make_rsrc(e + off, n), rs = make_rsrc(s + off, n), rr = make_rsrc(r + off, n);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t o = voff + u * kWave * kOctBytes<DT>;
+            buf.e[u] = load_oct<DT>(re, o);
+            buf.s[u] = load_oct<DT>(rs, o);
+            buf.r[u] = load_oct<DT>(rr, o);
+        }
+    }
+
+    __device__ __forceinline__ void process(const Buf &buf, int64_t b) const
+    {
+        const rsrc_t ro = make_rsrc(out + b * kBlockBytes, valid(b));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float fe[8], fs[8], fr[8], t[8];
+            widen<DT>(buf.e[u], fe);
+            widen<DT>(buf.s[u], fs);
+            widen<DT>(buf.r[u], fr);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t[i] = fe[i] + fs[i];
+            round_to<DT>(t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t[i] = fr[i] + t[i];
+            store_oct<DT>(ro, narrow<DT>(t), voff + u * kWave * kOctBytes<DT>);
+        }
+    }
+};
+
+template <int DT>
+__device__ __forceinline__ float load_scalar(const char *p, int64_t i)
+{
+    if constexpr (DT == DT_BF16)
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
+    else if constexpr (DT == DT_F16)
+        return (float)reinterpret_cast<const _Float16 *>(p)[i];
+    else
+        return reinterpret_cast<const float *>(p)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void store_scalar(char *p, int64_t i, float v)
+{
+    if constexpr (DT == DT_BF16)
+        reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    else if constexpr (DT == DT_F16)
+        reinterpret_cast<_Float16 *>(p)[i] = (_Float16)v;
+    else
+        reinterpret_cast<float *>(p)[i] = v;
+}
+
+template <int DT>
+__device__ __forceinline__ float round_scalar(float v)
+{
+    if constexpr (DT == DT_BF16)
+        return __uint_as_float(pack_bf16x2(v, 0.0f) << 16);
+    else if constexpr (DT == DT_F16)
+        return (float)(_Float16)v;
+    else
+        return v;
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void residual_add_kernel(const char *e, const char *s,
+                                                              const char *r, char *out,
+                                                              int64_t num_elements)
+{
+    const int64_t full_octs = num_elements / 8;
+    ResidualAddOp<DT, U> op{e, s, r, out, full_octs * kOctBytes<DT>,
+                            (uint32_t)lane_id() * kOctBytes<DT>};
+    const int64_t n_blocks = (full_octs + U * kWave - 1) / (U * kWave);
+    walk_blocks(op, n_blocks);
+    // the last num_elements % 8 elements: one lane each of the first wave
+    const int64_t tail = num_elements - full_octs * 8;
+    if (wave_id() == 0 && lane_id() < tail) {
+        const int64_t i = full_octs * 8 + lane_id();
+        const float t = round_scalar<DT>(load_scalar<DT>(e, i) + load_scalar<DT>(s, i));
+        store_scalar<DT>(out, i, load_scalar<DT>(r, i) + t);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Router-weight multiply
+// ---------------------------------------------------------------------------
+template <int XDT, int ODT, int U>
+struct RouterFwdOp {
+    struct Buf {
+        Oct x[U];
+    };
+    const char *x;
+    char *out;
+    int hidden;
+    uint32_t lane;
+
+    __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
+    {
+        const uint32_t row = (uint32_t)hidden * kElemBytes<XDT>;
+        const rsrc_t rx = chunk_rsrc(x + r * row, live ? row : 0u, (uint32_t)c * U * kWave * kOctBytes<XDT>);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            b.x[u] = load_oct<XDT>(rx, (lane + u * kWave) * kOctBytes<XDT>);
+    }
+
+    __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p) const
+    {
+        const uint32_t row = (uint32_t)hidden * kElemBytes<ODT>;
+        const rsrc_t ro = chunk_rsrc(out + r * row, slot >= 0 ? row : 0u,
+                                     (uint32_t)c * U * kWave * kOctBytes<ODT>);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[8];
+            widen<XDT>(b.x[u], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                f[i] = f[i] * p;
+            store_oct<ODT>(ro, narrow<ODT>(f), (lane + u * kWave) * kOctBytes<ODT>);
+        }
+    }
+};
+
+template <int XDT, int ODT, int U>
+__global__ __launch_bounds__(kBlock) void router_weight_fwd_kernel(const char *x, const float *probs,
+                                                                   char *out, int tokens, int hidden)
+{
+    const RowSchedule sched = make_schedule(tokens, nullptr, 0);
+    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
+    RouterFwdOp<XDT, ODT, U> op{x, out, hidden, (uint32_t)lane_id()};
+    walk_rows(op, sched, nullptr, probs, nch);
+}
+
+template <int XDT, int ODT, int U>
+struct RouterBwdOp {
+    struct Buf {
+        Oct g[U], x[U];
+    };
+    const char *g;
+    const char *x;
+    char *gx;
+    float *gp;
+    int hidden;
+    int nch;
+    uint32_t lane;
+    float acc;  // this lane's partial of the current row's probability gradient
+
+    __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
+    {
+        const uint32_t grow = (uint32_t)hidden * kElemBytes<ODT>, xrow = (uint32_t)hidden * kElemBytes<XDT>;
+        const rsrc_t rg = chunk_rsrc(g + r * grow, live ? grow : 0u, (uint32_t)c * U * kWave * kOctBytes<ODT>);
+        // x is read only for the probability gradient
+        const rsrc_t rx = chunk_rsrc(x + r * xrow, live && gp ? xrow : 0u, (uint32_t)c * U * kWave * kOctBytes<XDT>);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            b.g[u] = load_oct<ODT>(rg, (lane + u * kWave) * kOctBytes<ODT>);
+            b.x[u] = load_oct<XDT>(rx, (lane + u * kWave) * kOctBytes<XDT>);
+        }
+    }
+
+    __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p)
+    {
+        const uint32_t xrow = (uint32_t)hidden * kElemBytes<XDT>;
+        const rsrc_t rgx = chunk_rsrc(gx + r * xrow, slot >= 0 && gx ? xrow : 0u,
+                                      (uint32_t)c * U * kWave * kOctBytes<XDT>);
+        if (c == 0)
+            acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float fg[8], fx[8], d[8];
+            widen<ODT>(b.g[u], fg);
+            widen<XDT>(b.x[u], fx);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                d[i] = fg[i] * p;
+                acc += fg[i] * fx[i];
+            }
+            store_oct<XDT>(rgx, narrow<XDT>(d), (lane + u * kWave) * kOctBytes<XDT>);
+        }
+        if (c == nch - 1 && slot >= 0 && gp) {
+            const float total = wave_sum(acc);
+            if (lane == 0)
+                gp[slot] = total;
+        }
+    }
+};
+
+template <int XDT, int ODT, int U>
+__global__ __launch_bounds__(kBlock) void router_weight_bwd_kernel(const char *g, const char *x,
+                                                                   const float *probs, char *gx,
+                                                                   float *gp, int tokens, int hidden)
+{
+    const RowSchedule sched = make_schedule(tokens, nullptr, 0);
+    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
+    RouterBwdOp<XDT, ODT, U> op{g, x, gx, gp, hidden, nch, (uint32_t)lane_id(), 0.0f};
+    walk_rows(op, sched, nullptr, probs, nch);
+}
+
+// ---------------------------------------------------------------------------
+// Squared ReLU x probs
+// ---------------------------------------------------------------------------
+// tanh in fp32 from its odd Taylor series below |z| = 0.5 (the first omitted term,
+// 929569 z^15 / 638512875, is under 1e-7 relative there) and from
+// (1 - t) / (1 + t), t = e^(-2|z|), above, where 1 - t >= 0.63 cancels nothing.
+__device__ __forceinline__ float tanh_f32(float z)
+{
+    constexpr float c3 = -1.0f / 3.0f, c5 = 2.0f / 15.0f, c7 = -17.0f / 315.0f,
+                    c9 = 62.0f / 2835.0f, c11 = -1382.0f / 155925.0f, c13 = 21844.0f / 6081075.0f;
+    constexpr float kNeg2Log2e = -2.8853900817779268f;
+    const float a = __builtin_fabsf(z);
+    const float z2 = z * z;
+    const float poly = c3 + z2 * (c5 + z2 * (c7 + z2 * (c9 + z2 * (c11 + z2 * c13))));
+    const float small = z + z * (z2 * poly);
+    const float t = __builtin_amdgcn_exp2f(a * kNeg2Log2e);
+    const float large = __builtin_copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), z);
+    return a < 0.5f ? small : large;
+}
+
+template <int U, bool kClamp>
+struct SquaredReluOp {
+    struct Buf {
+        u32x4 x[U];
+    };
+    const uint16_t *x;
+    uint16_t *y;
+    int hidden;
+    float s, inv_s;
+    int zero_padding;
+    uint32_t voff;
+
+    __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
+    {
+        const uint32_t row = (uint32_t)hidden * 2u;
+        const rsrc_t rx = chunk_rsrc(x + r * hidden, live ? row : 0u, (uint32_t)c * U * kWave * kVecBytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            b.x[u] = load_vec(rx, voff + u * kWave * kVecBytes);
+    }
+
+    __device__ __forceinline__ float act(float v) const
+    {
+        if constexpr (kClamp) {
+            const float a = __builtin_elementwise_maximum(s * tanh_f32(v * inv_s), 0.0f);
+            return a * a;
+        } else {
+            const float a = __builtin_elementwise_maximum(v, 0.0f);
+            return a * a;
+        }
+    }
+
+    __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p) const
+    {
+        const uint32_t row = (uint32_t)hidden * 2u;
+        const rsrc_t ry = chunk_rsrc(y + r * hidden, (slot >= 0 || zero_padding) ? row : 0u,
+                                     (uint32_t)c * U * kWave * kVecBytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float a0 = act(bf16_lo(b.x[u][q])), a1 = act(bf16_hi(b.x[u][q]));
+                if constexpr (!kClamp) {
+                    // the square is materialised in bf16 before the probability multiply
+                    const unsigned sq = pack_bf16x2(a0, a1);
+                    a0 = bf16_lo(sq);
+                    a1 = bf16_hi(sq);
+                }
+                o[q] = pack_bf16x2(a0 * p, a1 * p);
+            }
+            store_vec(ry, o, voff + u * kWave * kVecBytes);
+        }
+    }
+};
+
+template <int U, bool kClamp>
+__global__ __launch_bounds__(kBlock) void squared_relu_probs_kernel(
+    const uint16_t *x, const float *probs, uint16_t *y, int rows, int hidden, float s, float inv_s,
+    const int *n_used, const int *perm, int zero_padding)
+{
+    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
+    SquaredReluOp<U, kClamp> op{x, y, hidden, s, inv_s, zero_padding, (uint32_t)lane_id() * kVecBytes};
+    walk_rows(op, sched, perm, probs, nch);
+}
+
+// ---------------------------------------------------------------------------
+// Token-local unpermute in fixed expert order
+// ---------------------------------------------------------------------------
+// One wave per output token (a fixed grid striding over tokens), lanes over the
+// hidden dimension in chunks of U octs. The token's map entries sit one per lane and
+// are broadcast with v_readlane. Contributions are loaded G experts at a time, all G
+// issued before any is added; an expert with no contribution gets an empty buffer
+// resource, which reads +0 without touching memory, and adding +0 to the running
+// sum changes no bit (the sum starts at +0 and can never be -0). The adds then run
+// in increasing expert id.
+template <int ODT, int U, int G>
+__global__ __launch_bounds__(kBlock) void unpermute_kernel(const uint16_t *eo, int64_t erows,
+                                                           const int *map, const int *valid_tokens,
+                                                           char *out, int tokens, int hidden, int E)
+{
+    const int lane = lane_id();
+    const int64_t W = (int64_t)gridDim.x * kWavesPerBlock;
+    int bound = tokens;
+    if (valid_tokens) {
+        const int v = *valid_tokens;
+        bound = v < 0 ? 0 : (v > tokens ? tokens : v);
+    }
+    const uint32_t row = (uint32_t)hidden * 2u;
+    const uint32_t orow = (uint32_t)hidden * kElemBytes<ODT>;
+    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
+    for (int64_t t = wave_id(); t < bound; t += W) {
+        for (int c = 0; c < nch; ++c) {
+            float acc[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[u][i] = 0.0f;
+            for (int e0 = 0; e0 < E; e0 += kWave) {
+                const int ne = E - e0 < kWave ? E - e0 : kWave;
+                const int mv = lane < ne ? map[t * E + e0 + lane] : -1;
+                for (int g0 = 0; g0 < ne; g0 += G) {
+                    u32x4 buf[G][U];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int m = g0 + g < ne ? __builtin_amdgcn_readlane(mv, g0 + g) : -1;
+                        const bool ok = m >= 0 && m < erows;
+                        const rsrc_t rs = chunk_rsrc(eo + (int64_t)(ok ? m : 0) * hidden, ok ? row : 0u,
+                                                     (uint32_t)c * U * kWave * kVecBytes);
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            buf[g][u] = load_vec(rs, (lane + u * kWave) * kVecBytes);
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                acc[u][2 * q] = acc[u][2 * q] + bf16_lo(buf[g][u][q]);
+                                acc[u][2 * q + 1] = acc[u][2 * q + 1] + bf16_hi(buf[g][u][q]);
+                            }
+                }
+            }
+            const rsrc_t ro = chunk_rsrc(out + t * orow, orow, (uint32_t)c * U * kWave * kOctBytes<ODT>);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                store_oct<ODT>(ro, narrow<ODT>(acc[u]), (lane + u * kWave) * kOctBytes<ODT>);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+thread_local int t_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    int cus = 0;
+};
+DeviceInfo g_devices[kMaxDevices];
+
+hipError_t device_cus(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    DeviceInfo &d = g_devices[dev];
+    std::call_once(d.once, [&d, dev] {
+        hipDeviceProp_t prop;
+        d.err = hipGetDeviceProperties(&prop, dev);
+        if (d.err == hipSuccess)
+            d.cus = prop.multiProcessorCount;
+    });
+    *cus = d.cus;
+    return d.err;
+}
+
+moe_status_t fail_hip(hipError_t e)
+{
+    t_last_hip_error = (int)e;
+    return MOE_ERR_HIP;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+Range span(const void *p, uint64_t bytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, p ? a + (uintptr_t)bytes : a};
+}
+bool overlap(Range a, Range b) { return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int elem_bytes(moe_dtype_t d) { return d == MOE_FP32 ? 4 : 2; }
+bool dtype_ok(moe_dtype_t d) { return d == MOE_BF16 || d == MOE_FP16 || d == MOE_FP32; }
+
+constexpr int64_t kMaxRows = 0x7fffffffLL - 64LL * 65536LL;
+constexpr int64_t kMaxHidden = 1LL << 26;  // a row stays under 2^32 bytes in fp32
+
+int pick_u(int64_t octs)
+{
+    const int64_t u = (octs + kWave - 1) / kWave;
+    return u >= 4 ? 4 : (u < 1 ? 1 : (int)u);
+}
+
+moe_status_t launched()
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_OK : fail_hip(e);
+}
+
+// residual add dispatch ------------------------------------------------------
+template <int DT>
+void launch_residual(int blocks, hipStream_t st, const void *e, const void *s, const void *r, void *o,
+                     int64_t n)
+{
+    hipLaunchKernelGGL((residual_add_kernel<DT, 4>), dim3(blocks), dim3(kBlock), 0, st,
+                       static_cast<const char *>(e), static_cast<const char *>(s),
+                       static_cast<const char *>(r), static_cast<char *>(o), n);
+}
+
+// router weight dispatch -----------------------------------------------------
+template <int XDT, int ODT, int U>
+void launch_router_fwd_u(int blocks, hipStream_t st, const void *x, const float *p, void *o, int t, int h)
+{
+    hipLaunchKernelGGL((router_weight_fwd_kernel<XDT, ODT, U>), dim3(blocks), dim3(kBlock), 0, st,
+                       static_cast<const char *>(x), p, static_cast<char *>(o), t, h);
+}
+
+template <int XDT, int ODT>
+void launch_router_fwd(int U, int blocks, hipStream_t st, const void *x, const float *p, void *o, int t, int h)
+{
+    switch (U) {
+    case 1: launch_router_fwd_u<XDT, ODT, 1>(blocks, st, x, p, o, t, h); break;
+    case 2: launch_router_fwd_u<XDT, ODT, 2>(blocks, st, x, p, o, t, h); break;
+    case 3: launch_router_fwd_u<XDT, ODT, 3>(blocks, st, x, p, o, t, h); break;
+    default: launch_router_fwd_u<XDT, ODT, 4>(blocks, st, x, p, o, t, h); break;
+    }
+}
+
+template <int XDT, int ODT, int U>
+void launch_router_bwd_u(int blocks, hipStream_t st, const void *g, const void *x, const float *p, void *gx,
+                         float *gp, int t, int h)
+{
+    hipLaunchKernelGGL((router_weight_bwd_kernel<XDT, ODT, U>), dim3(blocks), dim3(kBlock), 0, st,
+                       static_cast<const char *>(g), static_cast<const char *>(x), p,
+                       static_cast<char *>(gx), gp, t, h);
+}
+
+template <int XDT, int ODT>
+void launch_router_bwd(int U, int blocks, hipStream_t st, const void *g, const void *x, const float *p,
+                       void *gx, float *gp, int t, int h)
+{
+    switch (U) {
+    case 1: launch_router_bwd_u<XDT, ODT, 1>(blocks, st, g, x, p, gx, gp, t, h); break;
+    case 2: launch_router_bwd_u<XDT, ODT, 2>(blocks, st, g, x, p, gx, gp, t, h); break;
+    case 3: launch_router_bwd_u<XDT, ODT, 3>(blocks, st, g, x, p, gx, gp, t, h); break;
+    default: launch_router_bwd_u<XDT, ODT, 4>(blocks, st, g, x, p, gx, gp, t, h); break;
+    }
+}
+
+// squared relu dispatch ------------------------------------------------------
+template <int U, bool C>
+void launch_sqrelu_u(int blocks, hipStream_t st, const uint16_t *x, const float *p, uint16_t *y, int rows,
+                     int hidden, float s, float inv_s, const int *nu, const int *pm, int zp)
+{
+    hipLaunchKernelGGL((squared_relu_probs_kernel<U, C>), dim3(blocks), dim3(kBlock), 0, st, x, p, y, rows,
+                       hidden, s, inv_s, nu, pm, zp);
+}
+
+template <bool C>
+void launch_sqrelu(int U, int blocks, hipStream_t st, const uint16_t *x, const float *p, uint16_t *y,
+                   int rows, int hidden, float s, float inv_s, const int *nu, const int *pm, int zp)
+{
+    switch (U) {
+    case 1: launch_sqrelu_u<1, C>(blocks, st, x, p, y, rows, hidden, s, inv_s, nu, pm, zp); break;
+    case 2: launch_sqrelu_u<2, C>(blocks, st, x, p, y, rows, hidden, s, inv_s, nu, pm, zp); break;
+    case 3: launch_sqrelu_u<3, C>(blocks, st, x, p, y, rows, hidden, s, inv_s, nu, pm, zp); break;
+    default: launch_sqrelu_u<4, C>(blocks, st, x, p, y, rows, hidden, s, inv_s, nu, pm, zp); break;
+    }
+}
+
+// unpermute: G experts per batch of loads, U octs per lane per chunk
+constexpr int kUnpermuteU = 2;
+constexpr int kUnpermuteG = 4;
+// The unpermute waits on each group of gathers before adding it, so it keeps more
+// waves resident than the pure streams do.
+constexpr int kUnpermuteBlocksPerCU = 4;
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+moe_status_t moe_residual_add(const void *expert_output, const void *shared_expert_output,
+                              const void *residual, void *output, int64_t num_elements,
+                              moe_dtype_t dtype, hipStream_t stream, int num_workgroups)
+{
+    if (num_elements < 0 || !dtype_ok(dtype) || num_workgroups < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (num_elements == 0)
+        return MOE_OK;
+    if (!expert_output || !shared_expert_output || !residual || !output)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(expert_output, 16) || !aligned(shared_expert_output, 16) || !aligned(residual, 16) ||
+        !aligned(output, 16))
+        return MOE_ERR_ALIGNMENT;
+    const uint64_t bytes = (uint64_t)num_elements * elem_bytes(dtype);
+    const Range o = span(output, bytes);
+    for (const void *in : {expert_output, shared_expert_output, residual})
+        if (in != output && overlap(o, span(in, bytes)))
+            return MOE_ERR_INVALID_ARG;
+    int cus = 0;
+    hipError_t he = device_cus(&cus);
+    if (he != hipSuccess)
+        return fail_hip(he);
+    const int64_t octs = num_elements / 8;
+    const int64_t n_blocks = (octs + 4 * kWave - 1) / (4 * kWave);
+    const int blocks = num_workgroups > 0 ? num_workgroups : balanced_workgroups(n_blocks, cus, 1);
+    switch (dtype) {
+    case MOE_BF16: launch_residual<DT_BF16>(blocks, stream, expert_output, shared_expert_output, residual, output, num_elements); break;
+    case MOE_FP16: launch_residual<DT_F16>(blocks, stream, expert_output, shared_expert_output, residual, output, num_elements); break;
+    default: launch_residual<DT_F32>(blocks, stream, expert_output, shared_expert_output, residual, output, num_elements); break;
+    }
+    return launched();
+}
+
+moe_status_t moe_router_weight_fwd(const void *x, moe_dtype_t x_dtype, const float *probs,
+                                   void *out, moe_dtype_t out_dtype, int64_t tokens,
+                                   int64_t hidden, hipStream_t stream, int num_workgroups)
+{
+    if (tokens < 0 || hidden <= 0 || tokens > kMaxRows || hidden > kMaxHidden || num_workgroups < 0 ||
+        !dtype_ok(x_dtype) || !(out_dtype == x_dtype || out_dtype == MOE_FP32))
+        return MOE_ERR_INVALID_ARG;
+    if (hidden % 8 != 0)
+        return MOE_ERR_ALIGNMENT;
+    if (tokens == 0)
+        return MOE_OK;
+    if (!x || !probs || !out)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(probs, 4))
+        return MOE_ERR_ALIGNMENT;
+    const uint64_t T = (uint64_t)tokens, H = (uint64_t)hidden;
+    const Range o = span(out, T * H * elem_bytes(out_dtype));
+    if (overlap(o, span(x, T * H * elem_bytes(x_dtype))) || overlap(o, span(probs, T * 4)))
+        return MOE_ERR_INVALID_ARG;
+    int cus = 0;
+    hipError_t he = device_cus(&cus);
+    if (he != hipSuccess)
+        return fail_hip(he);
+    const int U = pick_u(hidden / 8);
+    const int blocks = num_workgroups > 0 ? num_workgroups : balanced_workgroups(tokens, cus, 1);
+    const int t = (int)tokens, h = (int)hidden;
+    if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_BF16>(U, blocks, stream, x, probs, out, t, h);
+    else if (x_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_F32>(U, blocks, stream, x, probs, out, t, h);
+    else if (x_dtype == MOE_FP16 && out_dtype == MOE_FP16) launch_router_fwd<DT_F16, DT_F16>(U, blocks, stream, x, probs, out, t, h);
+    else if (x_dtype == MOE_FP16) launch_router_fwd<DT_F16, DT_F32>(U, blocks, stream, x, probs, out, t, h);
+    else launch_router_fwd<DT_F32, DT_F32>(U, blocks, stream, x, probs, out, t, h);
+    return launched();
+}
+
+moe_status_t moe_router_weight_bwd(const void *grad_out, moe_dtype_t out_dtype, const void *x,
+                                   moe_dtype_t x_dtype, const float *probs, void *grad_x,
+                                   float *grad_probs, int64_t tokens, int64_t hidden,
+                                   hipStream_t stream, int num_workgroups)
+{
+    if (tokens < 0 || hidden <= 0 || tokens > kMaxRows || hidden > kMaxHidden || num_workgroups < 0 ||
+        !dtype_ok(x_dtype) || !(out_dtype == x_dtype || out_dtype == MOE_FP32))
+        return MOE_ERR_INVALID_ARG;
+    if (hidden % 8 != 0)
+        return MOE_ERR_ALIGNMENT;
+    if (tokens == 0)
+        return MOE_OK;
+    if (!grad_out || !probs || (grad_probs && !x))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(grad_out, 16) || !aligned(x, 16) || !aligned(grad_x, 16) || !aligned(probs, 4) ||
+        !aligned(grad_probs, 4))
+        return MOE_ERR_ALIGNMENT;
+    const uint64_t T = (uint64_t)tokens, H = (uint64_t)hidden;
+    const Range ins[] = {span(grad_out, T * H * elem_bytes(out_dtype)), span(x, T * H * elem_bytes(x_dtype)),
+                         span(probs, T * 4)};
+    const Range outs[] = {span(grad_x, T * H * elem_bytes(x_dtype)), span(grad_probs, T * 4)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i))
+                return MOE_ERR_INVALID_ARG;
+    if (overlap(outs[0], outs[1]))
+        return MOE_ERR_INVALID_ARG;
+    if (!grad_x && !grad_probs)
+        return MOE_OK;
+    int cus = 0;
+    hipError_t he = device_cus(&cus);
+    if (he != hipSuccess)
+        return fail_hip(he);
+    const int U = pick_u(hidden / 8);
+    const int blocks = num_workgroups > 0 ? num_workgroups : balanced_workgroups(tokens, cus, 1);
+    const int t = (int)tokens, h = (int)hidden;
+    if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_BF16>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else if (x_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else if (x_dtype == MOE_FP16 && out_dtype == MOE_FP16) launch_router_bwd<DT_F16, DT_F16>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else if (x_dtype == MOE_FP16) launch_router_bwd<DT_F16, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else launch_router_bwd<DT_F32, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    return launched();
+}
+
+moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, uint16_t *y,
+                                        int64_t rows, int64_t hidden, int clamp,
+                                        float clamp_scale, const int32_t *n_used,
+                                        const int32_t *permutation_map, int zero_padding,
+                                        hipStream_t stream, int num_workgroups)
+{
+    if (rows < 0 || hidden <= 0 || rows > kMaxRows || hidden > kMaxHidden || num_workgroups < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (clamp && !(clamp_scale > 0.0f && std::isfinite(clamp_scale)))
+        return MOE_ERR_INVALID_ARG;
+    if (hidden % 8 != 0)
+        return MOE_ERR_ALIGNMENT;
+    if (rows == 0)
+        return MOE_OK;
+    if (!x || !probs || !y)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(probs, 4) || !aligned(n_used, 4) ||
+        !aligned(permutation_map, 4))
+        return MOE_ERR_ALIGNMENT;
+    const uint64_t R = (uint64_t)rows, H = (uint64_t)hidden;
+    const Range o = span(y, R * H * 2);
+    const Range ins[] = {span(x, R * H * 2), span(probs, R * 4), span(n_used, 4), span(permutation_map, R * 4)};
+    for (const Range &i : ins)
+        if (overlap(o, i))
+            return MOE_ERR_INVALID_ARG;
+    int cus = 0;
+    hipError_t he = device_cus(&cus);
+    if (he != hipSuccess)
+        return fail_hip(he);
+    const int U = pick_u(hidden / 8);
+    const int blocks = num_workgroups > 0 ? num_workgroups : balanced_workgroups(rows, cus, 1);
+    const float s = clamp ? clamp_scale : 1.0f;
+    if (clamp)
+        launch_sqrelu<true>(U, blocks, stream, x, probs, y, (int)rows, (int)hidden, s, 1.0f / s, n_used,
+                            permutation_map, zero_padding ? 1 : 0);
+    else
+        launch_sqrelu<false>(U, blocks, stream, x, probs, y, (int)rows, (int)hidden, s, 1.0f, n_used,
+                             permutation_map, zero_padding ? 1 : 0);
+    return launched();
+}
+
+moe_status_t moe_unpermute_expert_order(const uint16_t *expert_output, int64_t expert_rows,
+                                        const int32_t *inverse_map, const int32_t *valid_tokens,
+                                        void *out, moe_dtype_t out_dtype, int64_t tokens,
+                                        int64_t hidden, int num_local_experts, hipStream_t stream,
+                                        int num_workgroups)
+{
+    if (tokens < 0 || hidden <= 0 || expert_rows < 0 || tokens > kMaxRows || hidden > kMaxHidden ||
+        expert_rows > kMaxRows || num_local_experts < 1 || num_local_experts > 1024 ||
+        num_workgroups < 0 || !(out_dtype == MOE_FP32 || out_dtype == MOE_BF16))
+        return MOE_ERR_INVALID_ARG;
+    if (hidden % 8 != 0)
+        return MOE_ERR_ALIGNMENT;
+    if (tokens == 0)
+        return MOE_OK;
+    if (!inverse_map || !out || (expert_rows > 0 && !expert_output))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(expert_output, 16) || !aligned(out, 16) || !aligned(inverse_map, 4) ||
+        !aligned(valid_tokens, 4))
+        return MOE_ERR_ALIGNMENT;
+    const uint64_t T = (uint64_t)tokens, H = (uint64_t)hidden;
+    const Range o = span(out, T * H * elem_bytes(out_dtype));
+    const Range ins[] = {span(expert_output, (uint64_t)expert_rows * H * 2),
+                         span(inverse_map, T * (uint64_t)num_local_experts * 4), span(valid_tokens, 4)};
+    for (const Range &i : ins)
+        if (overlap(o, i))
+            return MOE_ERR_INVALID_ARG;
+    int cus = 0;
+    hipError_t he = device_cus(&cus);
+    if (he != hipSuccess)
+        return fail_hip(he);
+    int resident = kUnpermuteBlocksPerCU;
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : balanced_workgroups(tokens, cus * resident, 1);
+    if (out_dtype == MOE_FP32)
+        hipLaunchKernelGGL((unpermute_kernel<DT_F32, kUnpermuteU, kUnpermuteG>), dim3(blocks), dim3(kBlock), 0,
+                           stream, expert_output, expert_rows, inverse_map, valid_tokens,
+                           static_cast<char *>(out), (int)tokens, (int)hidden, num_local_experts);
+    else
+        hipLaunchKernelGGL((unpermute_kernel<DT_BF16, kUnpermuteU, kUnpermuteG>), dim3(blocks), dim3(kBlock), 0,
+                           stream, expert_output, expert_rows, inverse_map, valid_tokens,
+                           static_cast<char *>(out), (int)tokens, (int)hidden, num_local_experts);
+    return launched();
+}
+
+const char *moe_elementwise_status_string(moe_status_t status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer or row width not a multiple of 8";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int moe_elementwise_last_hip_error(void) { return t_last_hip_error; }
+
+int moe_elementwise_abi_version(void) { return MOE_ELEMENTWISE_ABI_VERSION; }
+
+}  // extern "C"

@@ -16,7 +16,8 @@ from memory_bound_elementwise_amd import build as mbuild
 from memory_bound_elementwise_amd import load_library
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER_TO_LIB = {"swiglu_probs.h": "swiglu_probs", "hbm_probe.h": "hbm_probe"}
+HEADER_TO_LIB = {"swiglu_probs.h": "swiglu_probs", "hbm_probe.h": "hbm_probe",
+                 "moe_elementwise.h": "moe_elementwise"}
 
 
 def declared_functions(header: str):
@@ -139,3 +140,36 @@ def test_probe_validation(built):
     assert so.hbm_probe_stream(s, 1, d, 3, 4, 0, None) == 1
     d2 = (ctypes.c_void_p * 1)(A16 + 16)
     assert so.hbm_probe_stream(s, 1, d2, 1, 4, 0, None) == 1   # overlap
+
+
+def test_moe_validation():
+    from memory_bound_elementwise_amd.moe_elementwise import load_library as load_moe
+    lib = load_moe()
+    a, b, c, d = A16, A16 + (1 << 24), A16 + (2 << 24), A16 + (3 << 24)
+    assert lib.moe_residual_add(a, b, c, d, 0, 0, None, 0) == 0           # empty: no launch
+    assert lib.moe_residual_add(a, b, c, d, -1, 0, None, 0) == 1
+    assert lib.moe_residual_add(a, b, c, d, 8, 7, None, 0) == 1            # bad dtype
+    assert lib.moe_residual_add(a + 2, b, c, d, 8, 0, None, 0) == 2
+    assert lib.moe_residual_add(a, b, c, a + 16, 64, 0, None, 0) == 1      # partial overlap
+    assert lib.moe_residual_add(None, b, c, d, 8, 0, None, 0) == 1
+    f = lib.moe_router_weight_fwd
+    assert f(a, 0, b, c, 0, 0, 8, None, 0) == 0
+    assert f(a, 0, b, c, 1, 4, 8, None, 0) == 1                           # out must be x's type or fp32
+    assert f(a, 0, b, c, 2, 4, 12, None, 0) == 2                          # hidden % 8
+    assert f(a, 0, b + 2, c, 2, 4, 8, None, 0) == 2
+    assert f(a, 0, b, a, 0, 4, 8, None, 0) == 1                           # out over x
+    g = lib.moe_router_weight_bwd
+    assert g(a, 0, None, 0, b, c, d, 4, 8, None, 0) == 1                  # grad_probs needs x
+    sq = lib.moe_squared_relu_probs_fwd
+    assert sq(a, b, c, 4, 8, 1, 0.0, None, None, 0, None, 0) == 1         # clamp needs scale > 0
+    assert sq(a, b, c, 4, 8, 1, float("inf"), None, None, 0, None, 0) == 1
+    assert sq(a, b, c, 4, 8, 1, float("nan"), None, None, 0, None, 0) == 1
+    assert sq(a, b, c, 0, 8, 0, 0.0, None, None, 0, None, 0) == 0
+    assert sq(a, b, a, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1
+    u = lib.moe_unpermute_expert_order
+    assert u(a, 10, b, None, c, 2, 0, 8, 4, None, 0) == 0
+    assert u(a, 10, b, None, c, 1, 4, 8, 4, None, 0) == 1                 # fp16 out not supported
+    assert u(a, 10, b, None, c, 2, 4, 8, 0, None, 0) == 1                 # no experts
+    assert u(a, 10, b, None, c, 2, 4, 8, 2000, None, 0) == 1
+    assert u(a, 10, b + 1, None, c, 2, 4, 8, 4, None, 0) == 2
+    assert lib.moe_elementwise_abi_version() == 1

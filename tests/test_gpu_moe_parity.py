@@ -1,0 +1,259 @@
+"""MoE elementwise operations: HIP path (through the C ABI) vs the MoE-ops oracle.
+
+Bars: bitwise where the pages fix the result exactly (residual add = two unfused
+adds; router-weight forward and grad_x = one fp32 product and one rounding;
+squared ReLU without the soft clamp; unpermute = a fixed-order fp32 sum);
+within 1 bf16 ulp for the soft-clamped squared ReLU (tanh is evaluated by
+different fp32 formulas); grad_probs on the row-scale criterion.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe as moe_oracle
+from bf16cmp import assert_within_ulp, grad_probs_violations
+from memory_bound_elementwise_amd import (FusedMoEResidualAdd, RouterWeightMul, moe_residual_add,
+                                          moe_router_weight_bwd, moe_router_weight_fwd,
+                                          moe_squared_relu_probs_fwd, moe_unpermute_expert_order)
+from memory_bound_elementwise_amd.moe_elementwise import load_library
+from parity import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _rand(shape, dt, rng, scale=1.0, specials=True):
+    v = (rng.standard_normal(shape) * scale).astype(np.float32)
+    if specials and v.size >= 64:
+        flat = v.reshape(-1)
+        idx = rng.choice(flat.size, size=6 * max(1, flat.size // 500), replace=False)
+        k = idx.size // 6
+        flat[idx[:k]], flat[idx[k:2 * k]], flat[idx[2 * k:3 * k]] = np.inf, -np.inf, np.nan
+        flat[idx[3 * k:4 * k]], flat[idx[4 * k:5 * k]] = 0.0, -0.0
+        flat[idx[5 * k:]] = 65000.0 if dt == "f16" else 3e38
+    t = torch.from_numpy(v).to(TD[dt])
+    return t.numpy() if dt == "f32" else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _dev(a, dt):
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if dt != "f32" else np.ascontiguousarray(a))
+    return (t if dt == "f32" else t.view(TD[dt])).to(DEV)
+
+
+def _host(t, dt):
+    t = t.cpu()
+    return t.numpy() if dt == "f32" else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _same(a, b, dt):
+    if dt == "f32":
+        return np.array_equal(a.view(np.uint32), b.view(np.uint32)) or \
+            bool(np.all((a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))))
+    mant, expo = (0x7F, 0x7F80) if dt == "bf16" else (0x3FF, 0x7C00)
+    na = ((a & expo) == expo) & ((a & mant) != 0)
+    nb = ((b & expo) == expo) & ((b & mant) != 0)
+    return bool(np.all((a == b) | (na & nb)))
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 4096 * 7 + 5, 1 << 22])
+def test_residual_add(dt, n):
+    rng = np.random.default_rng(n)
+    e, s, r = _rand(n, dt, rng, 4.0), _rand(n, dt, rng, 4.0), _rand(n, dt, rng, 50.0)
+    want = moe_oracle.get().residual_add(e, s, r, dt)
+    out = torch.empty(n, dtype=TD[dt], device=DEV)
+    moe_residual_add(_dev(e, dt), _dev(s, dt), _dev(r, dt), out)
+    torch.cuda.synchronize()
+    assert _same(_host(out, dt), want, dt), f"residual add {dt} n={n}"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_residual_add_in_place_and_grid(dt):
+    rng = np.random.default_rng(5)
+    n = 3 * 2048 * 61 + 3
+    e, s, r = _rand(n, dt, rng), _rand(n, dt, rng), _rand(n, dt, rng, 10.0)
+    want = moe_oracle.get().residual_add(e, s, r, dt)
+    for nwg in (0, 1, 7, 1000):
+        res = _dev(r, dt)
+        moe_residual_add(_dev(e, dt), _dev(s, dt), res, res, num_workgroups=nwg)   # in place
+        torch.cuda.synchronize()
+        assert _same(_host(res, dt), want, dt), f"in place, {nwg} workgroups"
+
+
+def test_residual_add_autograd():
+    x = [torch.randn(64, 96, device=DEV, dtype=torch.bfloat16, requires_grad=True) for _ in range(3)]
+    y = FusedMoEResidualAdd.apply(*x)
+    ref = x[2].detach() + (x[0].detach() + x[1].detach())
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    g = torch.randn_like(y)
+    y.backward(g)
+    assert all(torch.equal(t.grad, g) for t in x)
+
+
+# ---------------------------------------------------------------------------
+ROUTER_TYPES = [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32"), ("f32", "f32")]
+
+
+@pytest.mark.parametrize("x_dt,out_dt", ROUTER_TYPES)
+@pytest.mark.parametrize("tokens,hidden", [(1, 8), (333, 520), (1027, 2048), (64, 7168 + 8)])
+def test_router_weight(x_dt, out_dt, tokens, hidden):
+    rng = np.random.default_rng(tokens + hidden)
+    x = _rand((tokens, hidden), x_dt, rng, 3.0, specials=False)
+    g = _rand((tokens, hidden), out_dt, rng, 1.0, specials=False)
+    p = rng.uniform(0, 1, tokens).astype(np.float32)
+    orc = moe_oracle.get()
+    out = torch.empty((tokens, hidden), dtype=TD[out_dt], device=DEV)
+    dp = torch.from_numpy(p).to(DEV)
+    moe_router_weight_fwd(_dev(x, x_dt), dp, out)
+    gx = torch.empty((tokens, hidden), dtype=TD[x_dt], device=DEV)
+    gp = torch.full((tokens,), -7.0, device=DEV)
+    moe_router_weight_bwd(_dev(g, out_dt), _dev(x, x_dt), dp, gx, gp)
+    torch.cuda.synchronize()
+    assert _same(_host(out, out_dt), orc.router_weight_fwd(x, x_dt, p, out_dt), out_dt), "router fwd"
+    ref = orc.router_weight_bwd(g, out_dt, x, x_dt, p)
+    assert _same(_host(gx, x_dt), ref["grad_x"], x_dt), "router grad_x"
+    bad = grad_probs_violations(gp.cpu().numpy(), ref["grad_probs_f64"], ref["row_scale"])
+    assert bad.size == 0, f"router grad_probs: {bad.size} rows off"
+
+
+def test_router_weight_optional_outputs():
+    rng = np.random.default_rng(9)
+    x = _rand((100, 512), "bf16", rng, specials=False)
+    g = _rand((100, 512), "bf16", rng, specials=False)
+    p = torch.from_numpy(rng.uniform(0, 1, 100).astype(np.float32)).to(DEV)
+    ref = moe_oracle.get().router_weight_bwd(g, "bf16", x, "bf16", p.cpu().numpy())
+    gx = torch.empty((100, 512), dtype=torch.bfloat16, device=DEV)
+    moe_router_weight_bwd(_dev(g, "bf16"), None, p, gx, None, x_dtype="bf16")   # x not needed
+    gp = torch.empty(100, device=DEV)
+    moe_router_weight_bwd(_dev(g, "bf16"), _dev(x, "bf16"), p, None, gp)
+    torch.cuda.synchronize()
+    assert _same(_host(gx, "bf16"), ref["grad_x"], "bf16")
+    assert grad_probs_violations(gp.cpu().numpy(), ref["grad_probs_f64"], ref["row_scale"]).size == 0
+
+
+def test_router_weight_autograd_and_grid():
+    x = torch.randn(300, 1024, device=DEV, dtype=torch.bfloat16, requires_grad=True)
+    p = torch.rand(300, 1, device=DEV, requires_grad=True)
+    y = RouterWeightMul.apply(x, p, torch.bfloat16)
+    assert torch.equal(y.view(torch.int16), (x.detach().float() * p.detach()).to(torch.bfloat16).view(torch.int16))
+    g = torch.randn_like(y)
+    y.backward(g)
+    assert torch.equal(x.grad.view(torch.int16), (g.float() * p.detach()).to(torch.bfloat16).view(torch.int16))
+    exact = (g.double() * x.detach().double()).sum(-1)
+    scale = (g.double() * x.detach().double()).abs().sum(-1)
+    assert torch.all((p.grad.reshape(-1).double() - exact).abs() <= 1e-6 + 1e-5 * scale)
+    outs = []
+    for nwg in (0, 1, 5, 999):
+        o = torch.empty(300, 1024, device=DEV)
+        gp = torch.empty(300, device=DEV)
+        moe_router_weight_fwd(x.detach(), p.detach().reshape(-1), o, num_workgroups=nwg)
+        moe_router_weight_bwd(g, x.detach(), p.detach().reshape(-1), None, gp, num_workgroups=nwg)
+        outs.append((o.clone(), gp.clone()))
+    for o, gp in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(gp.view(torch.int32), outs[0][1].view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+def _sq_run(x, p, **kw):
+    rows, hidden = x.shape
+    y = torch.full((rows, hidden), -1, dtype=torch.int16, device=DEV)
+    nu = kw.pop("n_used", None)
+    pm = kw.pop("permutation_map", None)
+    moe_squared_relu_probs_fwd(_dev(x, "bf16").view(torch.int16), torch.from_numpy(p).to(DEV), y,
+                               n_used=None if nu is None else torch.tensor([nu], dtype=torch.int32, device=DEV),
+                               permutation_map=None if pm is None else torch.from_numpy(pm).to(DEV), **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 0.5, 4.0, 30.0])
+@pytest.mark.parametrize("rows,hidden", [(7, 8), (513, 1536), (2000, 2048 + 8)])
+def test_squared_relu(clamp_scale, rows, hidden):
+    rng = np.random.default_rng(rows)
+    x = _rand((rows, hidden), "bf16", rng, 6.0)
+    p = rng.uniform(0, 1, rows).astype(np.float32)
+    got = _sq_run(x, p, clamp_scale=clamp_scale)
+    want = moe_oracle.get().squared_relu_probs(x, p, clamp_scale=clamp_scale)
+    if clamp_scale is None:
+        assert _same(got, want, "bf16"), "squared relu without clamp must be bit-exact"
+    else:
+        assert_within_ulp(got, want, 1, f"soft clamp s={clamp_scale}")
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 1.0, 8.0])
+def test_squared_relu_every_bf16_pattern(clamp_scale):
+    x = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    p = np.linspace(0.05, 1.0, 256).astype(np.float32)
+    got = _sq_run(x, p, clamp_scale=clamp_scale)
+    want = moe_oracle.get().squared_relu_probs(x, p, clamp_scale=clamp_scale)
+    if clamp_scale is None:
+        assert _same(got, want, "bf16")
+    else:
+        assert_within_ulp(got, want, 1, f"sweep s={clamp_scale}")
+
+
+@pytest.mark.parametrize("zero_padding", [False, True])
+def test_squared_relu_rows(zero_padding):
+    rng = np.random.default_rng(11)
+    rows, hidden = 4096, 1024
+    x = _rand((rows, hidden), "bf16", rng, 3.0, specials=False)
+    p = rng.uniform(0, 1, rows).astype(np.float32)
+    pm = rng.permutation(rows).astype(np.int32)
+    pm[rng.choice(rows, 40, replace=False)] = -1
+    for n_used in (0, 1, 3000, rows, rows + 9, -4):
+        kw = dict(clamp_scale=2.0, n_used=n_used, permutation_map=pm, zero_padding=zero_padding)
+        got = _sq_run(x, p, **kw)
+        want = moe_oracle.get().squared_relu_probs(x, p, **kw)
+        assert_within_ulp(got, want, 1, f"rows n_used={n_used}")
+        assert np.array_equal(got == 0xFFFF, want == 0xFFFF)
+
+
+# ---------------------------------------------------------------------------
+def _unpermute_inputs(rng, tokens, E, hidden, density):
+    valid = rng.random((tokens, E)) < density
+    # rows grouped by expert (the grouped GEMM's order), tokens in order within each
+    im = np.full((tokens, E), -1, np.int32)
+    row = 0
+    for e in range(E):
+        ts = np.flatnonzero(valid[:, e])
+        im[ts, e] = np.arange(row, row + ts.size)
+        row += ts.size
+    eo = _rand((max(row, 1), hidden), "bf16", rng, 1.0, specials=False)
+    return eo, im
+
+
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("tokens,E,hidden", [(1, 1, 8), (300, 4, 520), (2048, 8, 2048), (129, 70, 64),
+                                             (64, 300, 16)])
+def test_unpermute(out_dt, tokens, E, hidden):
+    rng = np.random.default_rng(tokens * E)
+    eo, im = _unpermute_inputs(rng, tokens, E, hidden, 0.5)
+    im[0, 0] = eo.shape[0] + 3        # an out-of-range entry contributes nothing
+    want = moe_oracle.get().unpermute(eo, im, out_dt)
+    out = torch.empty((tokens, hidden), dtype=TD[out_dt], device=DEV)
+    moe_unpermute_expert_order(_dev(eo, "bf16"), torch.from_numpy(im).to(DEV), out)
+    torch.cuda.synchronize()
+    assert _same(_host(out, out_dt), want, out_dt), "unpermute must be bit-exact (fixed order)"
+
+
+def test_unpermute_order_and_bound():
+    hidden = 64
+    big = np.zeros((3, hidden), np.uint16)
+    big[0], big[1], big[2] = 0x4B80, 0x3F80, 0xCB80          # 2^24, 1, -2^24
+    im = np.array([[0, 1, 2], [2, 1, 0], [1, -1, -1], [0, 2, 1]], np.int32)
+    out = torch.full((4, hidden), float("nan"), device=DEV)
+    vt = torch.tensor([3], dtype=torch.int32, device=DEV)
+    moe_unpermute_expert_order(_dev(big, "bf16"), torch.from_numpy(im).to(DEV), out, valid_tokens=vt)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[0] == 0.0) and np.all(o[1] == 1.0) and np.all(o[2] == 1.0)
+    assert np.all(np.isnan(o[3])), "token at valid_tokens must not be written"
+
+
+def test_moe_error_paths():
+    lib = load_library()
+    a = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    assert lib.moe_residual_add(a.data_ptr() + 2, a.data_ptr(), a.data_ptr(), a.data_ptr(), 8, 0, None, 0) == 2
+    say("[moe] error paths ok")

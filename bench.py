@@ -38,7 +38,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (fwd, bwd) and % of MI355X HBM peak at 1.1 GB shape"
-KERNEL_SRC = os.path.join(ROOT, "memory_bound_elementwise_amd", "csrc", "swiglu_probs.hip")
+CSRC = os.path.join(ROOT, "memory_bound_elementwise_amd", "csrc")
+KERNEL_SRC = [os.path.join(CSRC, "swiglu_probs.hip"), os.path.join(CSRC, "cdna4_stream.h")]
+MOE_SRC = [os.path.join(CSRC, "moe_elementwise.hip"), os.path.join(CSRC, "cdna4_stream.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "pmc_swiglu_probs_headline.json")
 
 
@@ -46,22 +48,25 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def kernel_source_hash(paths=None) -> str:
+    h = hashlib.sha256()
+    for p in (paths or KERNEL_SRC):
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per backward launch from the committed counter summary, or None when
-    it is missing, for another workload, or taken on another kernel source."""
+def measured_traffic(workload: str, key: str = "bwd", path: str = COUNTERS, sources=None):
+    """HBM bytes per launch of kernel `key` from a committed counter summary, or None
+    when it is missing, for another workload, or taken on other kernel sources."""
     try:
-        with open(COUNTERS) as fh:
+        with open(path) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("workload") != workload or d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("workload") != workload or d.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
-    return d.get("bwd", {}).get("hbm_bytes_per_launch")
+    return d.get(key, {}).get("hbm_bytes_per_launch")
 
 
 def cpu_model() -> str:
@@ -75,6 +80,162 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+
+MOE_OPS = {
+    "residual_add": "fused MoE residual add (bf16)",
+    "router_weight": "router-weight multiply, forward + backward (bf16)",
+    "squared_relu": "soft-clamped squared ReLU x probs (bf16)",
+    "unpermute": "token-local unpermute in expert order (bf16 in, fp32 out)",
+}
+
+
+def time_kernels(kernels, steps, warmup, cold_reps):
+    """kernels: list of (name, launch). Returns wall ms per step, per-kernel event
+    times (lists, ms) over the timed steps, and cold medians (ms) per kernel."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        for _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        for i, (_, fn) in enumerate(kernels):
+            fn()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, (name, _) in enumerate(kernels)}
+    cold = {}
+    if cold_reps > 0:
+        evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+        for name, fn in kernels:
+            ts = []
+            for _ in range(cold_reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                evict.sum(dtype=torch.int64)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            cold[name] = float(np.median(ts))
+        del evict
+    return wall, per, cold
+
+
+def bench_moe(args) -> int:
+    """One JSON line for one of the MoE elementwise operations (see MOE_OPS)."""
+    import numpy as np
+    import torch
+
+    import memory_bound_elementwise_amd as mbe
+    from memory_bound_elementwise_amd.workloads import make_moe_inputs, moe_algorithmic_bytes
+
+    op = args.op
+    dev = torch.device("cuda:0")
+    log(f"{op}: drawing inputs")
+    inp = make_moe_inputs(op, seed=0)
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if op == "residual_add":
+        e, sh, r = bits(inp["expert"]), bits(inp["shared"]), bits(inp["residual"])
+        out = torch.empty_like(r)
+        kernels = [("residual_add", lambda: mbe.moe_residual_add(e, sh, r, out))]
+        nbytes = {"residual_add": moe_algorithmic_bytes(op, inp)}
+        shape = {"tokens": r.shape[0], "hidden": r.shape[1]}
+    elif op == "router_weight":
+        x, g = bits(inp["x"]), bits(inp["grad_out"])
+        p = torch.from_numpy(inp["probs"]).to(dev)
+        out, gx = torch.empty_like(x), torch.empty_like(x)
+        gp = torch.empty_like(p)
+        kernels = [("fwd", lambda: mbe.moe_router_weight_fwd(x, p, out)),
+                   ("bwd", lambda: mbe.moe_router_weight_bwd(g, x, p, gx, gp))]
+        nbytes = {"fwd": moe_algorithmic_bytes(op, inp, "fwd"), "bwd": moe_algorithmic_bytes(op, inp, "bwd")}
+        shape = {"rows": x.shape[0], "hidden": x.shape[1]}
+    elif op == "squared_relu":
+        x = bits(inp["x"])
+        p = torch.from_numpy(inp["probs"]).to(dev)
+        y = torch.empty_like(x)
+        kernels = [("squared_relu", lambda: mbe.moe_squared_relu_probs_fwd(x, p, y, clamp_scale=inp["clamp_scale"]))]
+        nbytes = {"squared_relu": moe_algorithmic_bytes(op, inp)}
+        shape = {"rows": x.shape[0], "hidden": x.shape[1], "clamp_scale": inp["clamp_scale"]}
+    else:
+        eo = bits(inp["expert_output"])
+        im = torch.from_numpy(inp["inverse_map"]).to(dev)
+        out = torch.empty((im.shape[0], eo.shape[1]), dtype=torch.float32, device=dev)
+        kernels = [("unpermute", lambda: mbe.moe_unpermute_expert_order(eo, im, out))]
+        nbytes = {"unpermute": moe_algorithmic_bytes(op, inp)}
+        shape = {"tokens": im.shape[0], "local_experts": im.shape[1], "hidden": eo.shape[1],
+                 "routed_pairs": int((inp["inverse_map"] >= 0).sum())}
+
+    log(f"{op}: warm-up {args.warmup}, timing {args.steps} steps")
+    wall, per, cold = time_kernels(kernels, args.steps, args.warmup, args.cold_reps)
+    total = sum(nbytes.values())
+    value = total / (wall * 1e6)
+    kern = {}
+    for name, _ in kernels:
+        avg = float(np.mean(per[name]))
+        kern[name] = {"algorithmic_bytes": nbytes[name], "us": round(avg * 1e3, 2),
+                      "GB/s": round(nbytes[name] / (avg * 1e6), 1),
+                      "frac_of_peak": round(nbytes[name] / (avg * 1e6) / HBM_PEAK_GBS, 4)}
+        if name in cold:
+            kern[name]["cold_us"] = round(cold[name] * 1e3, 2)
+            kern[name]["cold_GB/s"] = round(nbytes[name] / (cold[name] * 1e6), 1)
+        log(f"{op} {name}: {kern[name]}")
+    dom = max(nbytes, key=nbytes.get)
+    traffic = measured_traffic(op, dom, os.path.join(ROOT, "profiles", f"pmc_moe_{op}.json"), MOE_SRC)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.moe as mo
+        orc = mo.get()
+        # a bounded sample: the oracle on a leading slice of the same inputs, ~cpu_seconds
+        frac = {"residual_add": 1.0, "router_weight": 0.125, "squared_relu": 0.25, "unpermute": 0.25}[op]
+        spent, reps, moved = 0.0, 0, 0
+        while reps < 1 or (spent < args.cpu_seconds and reps < 50):
+            t = time.perf_counter()
+            if op == "residual_add":
+                orc.residual_add(inp["expert"], inp["shared"], inp["residual"], "bf16")
+                moved += total
+            elif op == "router_weight":
+                n = int(inp["x"].shape[0] * frac)
+                orc.router_weight_fwd(inp["x"][:n], "bf16", inp["probs"][:n], "bf16")
+                orc.router_weight_bwd(inp["grad_out"][:n], "bf16", inp["x"][:n], "bf16", inp["probs"][:n])
+                moved += int(total * n / inp["x"].shape[0])
+            elif op == "squared_relu":
+                n = int(inp["x"].shape[0] * frac)
+                orc.squared_relu_probs(inp["x"][:n], inp["probs"][:n], clamp_scale=inp["clamp_scale"])
+                moved += int(total * n / inp["x"].shape[0])
+            else:
+                n = int(inp["inverse_map"].shape[0] * frac)
+                orc.unpermute(inp["expert_output"], inp["inverse_map"][:n], "f32")
+                moved += int(total * n / inp["inverse_map"].shape[0])
+            spent += time.perf_counter() - t
+            reps += 1
+        cpu = {"value": round(moved / (spent * 1e9), 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{'all' if frac == 1.0 else f'the first {frac:g} of the'} rows of the same "
+                         f"inputs x {reps} reps, {spent:.1f} s; {cpu_model()}"}
+        log(f"{op}: cpu baseline {cpu['value']} GB/s")
+
+    print(json.dumps({
+        "metric": f"achieved HBM GB/s of the {MOE_OPS[op]} and % of MI355X HBM peak",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"moe_{op}", **shape, "io_dtype": "bf16", "seed": 0},
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kern[dom]["frac_of_peak"], "traffic": traffic},
+        "cpu_baseline": cpu,
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +243,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
                     choices=["tiny", "mid", "headline", "padded", "edge"])
+    ap.add_argument("--op", default="swiglu_probs", choices=["swiglu_probs"] + sorted(MOE_OPS),
+                    help="swiglu_probs: the activation fwd+bwd (default); the others: the MoE "
+                         "elementwise operations next to it, at the headline MoE shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=10,
@@ -97,6 +261,9 @@ def main() -> int:
               f"mode (asked for --gpus {args.gpus}). Rows shard across GPUs with no exchange; "
               f"run one process per GPU instead.", file=sys.stderr)
         return 2
+
+    if args.op != "swiglu_probs":
+        return bench_moe(args)
 
     import numpy as np
     import torch

@@ -9,8 +9,10 @@
 //
 // All four are HBM-bound streams built on cdna4_stream.h: 128-bit buffer accesses
 // on per-row (or per-block) resources whose hardware range check masks ragged ends
-// and rows that are not live, nontemporal hints, one workgroup per CU, and the
-// two-buffer software pipeline per wave. Values are handled in groups of eight
+// and rows that are not live, nontemporal hints, and (residual add, router weight,
+// squared ReLU) the two-buffer software pipeline per wave. The pure streams launch
+// one workgroup per CU; the soft-clamped squared ReLU (arithmetic-heavy) and the
+// unpermute (gather-latency-bound) keep two per CU resident. Values are handled in groups of eight
 // elements per lane ("octs": one 16-byte access for 16-bit types, two for fp32).
 #include <hip/hip_runtime.h>
 
@@ -324,21 +326,20 @@ __global__ __launch_bounds__(kBlock) void router_weight_bwd_kernel(const char *g
 // ---------------------------------------------------------------------------
 // Squared ReLU x probs
 // ---------------------------------------------------------------------------
-// tanh in fp32 from its odd Taylor series below |z| = 0.5 (the first omitted term,
-// 929569 z^15 / 638512875, is under 1e-7 relative there) and from
-// (1 - t) / (1 + t), t = e^(-2|z|), above, where 1 - t >= 0.63 cancels nothing.
+// tanh in fp32 from its odd Taylor series below |z| = 0.3 (an alternating series
+// there: the first omitted term, 1382 z^11 / 155925, is under 5.4e-8 of tanh(z), less
+// than one fp32 ulp) and from (1 - t) / (1 + t), t = e^(-2|z|), above, where
+// 1 - t >= 0.45 cancels nothing.
 __device__ __forceinline__ float tanh_f32(float z)
 {
-    constexpr float c3 = -1.0f / 3.0f, c5 = 2.0f / 15.0f, c7 = -17.0f / 315.0f,
-                    c9 = 62.0f / 2835.0f, c11 = -1382.0f / 155925.0f, c13 = 21844.0f / 6081075.0f;
+    constexpr float c3 = -1.0f / 3.0f, c5 = 2.0f / 15.0f, c7 = -17.0f / 315.0f, c9 = 62.0f / 2835.0f;
     constexpr float kNeg2Log2e = -2.8853900817779268f;
     const float a = __builtin_fabsf(z);
     const float z2 = z * z;
-    const float poly = c3 + z2 * (c5 + z2 * (c7 + z2 * (c9 + z2 * (c11 + z2 * c13))));
-    const float small = z + z * (z2 * poly);
+    const float small = z + z * (z2 * (c3 + z2 * (c5 + z2 * (c7 + z2 * c9))));
     const float t = __builtin_amdgcn_exp2f(a * kNeg2Log2e);
     const float large = __builtin_copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), z);
-    return a < 0.5f ? small : large;
+    return a < 0.3f ? small : large;
 }
 
 template <int U, bool kClamp>
@@ -613,11 +614,25 @@ void launch_sqrelu(int U, int blocks, hipStream_t st, const uint16_t *x, const f
 }
 
 // unpermute: G experts per batch of loads, U octs per lane per chunk
-constexpr int kUnpermuteU = 2;
-constexpr int kUnpermuteG = 4;
+#ifndef MOE_UNPERMUTE_U
+#define MOE_UNPERMUTE_U 4
+#endif
+#ifndef MOE_UNPERMUTE_G
+#define MOE_UNPERMUTE_G 4
+#endif
+#ifndef MOE_UNPERMUTE_BPC
+#define MOE_UNPERMUTE_BPC 2
+#endif
+#ifndef MOE_SQRELU_BPC
+#define MOE_SQRELU_BPC 2
+#endif
+constexpr int kUnpermuteU = MOE_UNPERMUTE_U;
+constexpr int kUnpermuteG = MOE_UNPERMUTE_G;
 // The unpermute waits on each group of gathers before adding it, so it keeps more
 // waves resident than the pure streams do.
-constexpr int kUnpermuteBlocksPerCU = 4;
+constexpr int kUnpermuteBlocksPerCU = MOE_UNPERMUTE_BPC;
+// The soft-clamped squared ReLU spends ~20 VALU operations per element on tanh.
+constexpr int kSquaredReluBlocksPerCU = MOE_SQRELU_BPC;
 
 }  // namespace
 
@@ -767,7 +782,8 @@ moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, u
     if (he != hipSuccess)
         return fail_hip(he);
     const int U = pick_u(hidden / 8);
-    const int blocks = num_workgroups > 0 ? num_workgroups : balanced_workgroups(rows, cus, 1);
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : balanced_workgroups(rows, cus * kSquaredReluBlocksPerCU, 1);
     const float s = clamp ? clamp_scale : 1.0f;
     if (clamp)
         launch_sqrelu<true>(U, blocks, stream, x, probs, y, (int)rows, (int)hidden, s, 1.0f / s, n_used,

@@ -161,3 +161,77 @@ def make_inputs(w: Workload | str, seed: int = 0, rows: Optional[int] = None) ->
         "zero_padding": bool(w.zero_padding),
         "workload": w,
     }
+
+
+# ---------------------------------------------------------------------------
+# Workloads of the MoE elementwise operations next to the activation. Shapes follow
+# the headline activation workload: 53760 routed rows = 6720 tokens x top-8, a model
+# hidden size of 7168 beside the expert width of 2048, 8 local experts per GPU.
+# ---------------------------------------------------------------------------
+MOE_TOKENS = 6720
+MOE_TOPK = 8
+MOE_HIDDEN = 7168
+MOE_LOCAL_EXPERTS = 8
+
+
+def make_moe_inputs(op: str, seed: int = 0, scale: float = 1.0) -> dict:
+    """Seeded inputs for one MoE op. ``scale`` < 1 shrinks the token/row count (tests).
+
+    residual_add : expert, shared, residual bf16 [6720, 7168] ~ N(0,1) (residual N(0, 4^2))
+    router_weight: x bf16 [53760, 7168] ~ N(0,1), probs U(0,1), grad_out bf16 ~ N(0,1)
+    squared_relu : x bf16 [53760, 2048] ~ N(0, 3^2), probs U(0,1), soft clamp scale 4
+    unpermute    : 6720 tokens x 8 local experts, each (token, expert) pair routed with
+                   probability 1/2; expert_output bf16 [routed pairs, 7168] ~ N(0,1) in
+                   expert-major (grouped-GEMM) order; inverse_map int32 [6720, 8]
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    tokens = max(1, int(MOE_TOKENS * scale))
+    rows = tokens * MOE_TOPK
+
+    def bf16(shape, std=1.0):
+        t = torch.randn(*shape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return _bf16_bits(t)
+
+    if op == "residual_add":
+        return {"expert": bf16((tokens, MOE_HIDDEN)), "shared": bf16((tokens, MOE_HIDDEN)),
+                "residual": bf16((tokens, MOE_HIDDEN), 4.0)}
+    if op == "router_weight":
+        x = bf16((rows, MOE_HIDDEN))
+        probs = torch.rand(rows, generator=g, dtype=torch.float32).numpy()
+        return {"x": x, "probs": probs, "grad_out": bf16((rows, MOE_HIDDEN))}
+    if op == "squared_relu":
+        x = bf16((rows, 2048), 3.0)
+        probs = torch.rand(rows, generator=g, dtype=torch.float32).numpy()
+        return {"x": x, "probs": probs, "clamp_scale": 4.0}
+    if op == "unpermute":
+        valid = (torch.rand(tokens, MOE_LOCAL_EXPERTS, generator=g) < 0.5).numpy()
+        im = np.full((tokens, MOE_LOCAL_EXPERTS), -1, np.int32)
+        row = 0
+        for e in range(MOE_LOCAL_EXPERTS):
+            ts = np.flatnonzero(valid[:, e])
+            im[ts, e] = np.arange(row, row + ts.size, dtype=np.int32)
+            row += ts.size
+        return {"expert_output": bf16((max(row, 1), MOE_HIDDEN)), "inverse_map": im}
+    raise ValueError(op)
+
+
+def moe_algorithmic_bytes(op: str, inp: dict, direction: str = "fwd") -> int:
+    """Bytes one launch must move (each byte once)."""
+    if op == "residual_add":
+        return 4 * inp["expert"].size * 2
+    if op == "router_weight":
+        n, rows = inp["x"].size, inp["x"].shape[0]
+        if direction == "fwd":
+            return n * 2 + n * 2 + rows * 4                  # read x, write out, read probs
+        return n * 2 * 3 + rows * 8                          # read g and x, write grad_x; probs, grad_probs
+    if op == "squared_relu":
+        n, rows = inp["x"].size, inp["x"].shape[0]
+        return n * 2 * 2 + rows * 4
+    if op == "unpermute":
+        im = inp["inverse_map"]
+        contrib = int((im >= 0).sum())
+        hidden = inp["expert_output"].shape[1]
+        return contrib * hidden * 2 + im.shape[0] * hidden * 4 + im.size * 4   # fp32 out
+    raise ValueError(op)

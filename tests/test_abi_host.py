@@ -173,3 +173,30 @@ def test_moe_validation():
     assert u(a, 10, b, None, c, 2, 4, 8, 2000, None, 0) == 1
     assert u(a, 10, b + 1, None, c, 2, 4, 8, 4, None, 0) == 2
     assert lib.moe_elementwise_abi_version() == 1
+
+
+def test_headers_compile_as_c(tmp_path):
+    """The headers are plain C: a C11 translation unit includes them, takes every
+    declared function's address, and links against the libraries."""
+    import shutil
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no gcc")
+    names = []
+    for h in HEADER_TO_LIB:
+        names += declared_functions(os.path.join(ROOT, "include", h))
+    src = tmp_path / "abi_check.c"
+    src.write_text("#include \"swiglu_probs.h\"\n#include \"moe_elementwise.h\"\n#include \"hbm_probe.h\"\n"
+                   "#include <stdio.h>\ntypedef void (*fn_t)(void);\nstatic const fn_t table[] = {\n"
+                   + "".join(f"    (fn_t)&{n},\n" for n in names)
+                   + "};\nint main(void) {\n    unsigned n = 0;\n"
+                   "    for (unsigned i = 0; i < sizeof table / sizeof table[0]; ++i) n += table[i] != 0;\n"
+                   "    printf(\"%u\\n\", n);\n    return 0;\n}\n")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    libdir = os.path.dirname(mbuild.lib_path("swiglu_probs"))
+    cmd = [cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+           f"-I{ROOT}/include", "-isystem", f"{rocm}/include", str(src), "-o", str(tmp_path / "abi_check"),
+           f"-L{libdir}", "-lswiglu_probs", "-lmoe_elementwise", "-lhbm_probe",
+           f"-Wl,-rpath,{libdir}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]

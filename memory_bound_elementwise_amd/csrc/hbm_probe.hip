@@ -1,60 +1,83 @@
 // Plain streaming kernels (copy, 2:1 and 3:2 read:write) for the practical HBM
 // ceiling and for calibrating FETCH_SIZE / WRITE_SIZE. C ABI in hbm_probe.h.
-// Loads and stores carry the nontemporal hint and the default grid is one
-// workgroup per CU: the configuration that streamed fastest on MI355X.
+//
+// They move data the way the activation kernels do, minus the arithmetic: each
+// wave streams 4 KiB blocks of every source (64 lanes x 4 x 16-byte buffer loads
+// with the nontemporal hint), blocks interleaved across waves, through the same
+// two-buffer pipeline (the next block's loads issued before the current block's
+// stores), with one workgroup per CU. Destination vector i is the XOR of the source
+// vectors i.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 
+#include <mutex>
+
+#include "cdna4_stream.h"
 #include "hbm_probe.h"
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using namespace cdna4;
 
-constexpr int kBlock = 256;
-constexpr int kUnroll = 4;
+constexpr int kU = 4;
+constexpr uint32_t kBlockBytes = kU * kWave * kVecBytes;  // 4 KiB per stream per block
 
 struct Ptrs {
-    const u32x4 *src[3];
-    u32x4 *dst[2];
+    const char *src[3];
+    char *dst[2];
 };
 
-// Each wave moves blocks of kUnroll * 64 vectors (4 KiB) per stream, blocks
-// interleaved across waves (block b + k * waves); all loads of a block are issued
-// before its stores. This row-per-wave mapping with nontemporal loads and stores
-// streamed fastest on MI355X in steady back-to-back runs.
 template <int NS, int ND>
-__global__ __launch_bounds__(kBlock) void stream_kernel(Ptrs p, int64_t n_vec)
-{
-    constexpr int kWave = 64;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t waves = (int64_t)gridDim.x * (kBlock / kWave);
-    const int64_t w = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
-    const int64_t per_block = (int64_t)kUnroll * kWave;
-    const int64_t n_blocks = (n_vec + per_block - 1) / per_block;
-    for (int64_t b = w; b < n_blocks; b += waves) {
-        u32x4 v[kUnroll];
+struct StreamOp {
+    struct Buf {
+        u32x4 v[NS][kU];
+    };
+    Ptrs p;
+    int64_t bytes;
+    uint32_t voff;
+
+    __device__ __forceinline__ uint32_t valid(int64_t b) const
+    {
+        const int64_t left = bytes - b * kBlockBytes;
+        return left <= 0 ? 0u : (left < kBlockBytes ? (uint32_t)left : kBlockBytes);
+    }
+
+    __device__ __forceinline__ void load(Buf &buf, int64_t b, bool live) const
+    {
+        const uint32_t n = live ? valid(b) : 0u;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t i = b * per_block + u * kWave + lane;
-            v[u] = u32x4{0u, 0u, 0u, 0u};
-            if (i < n_vec) {
+        for (int s = 0; s < NS; ++s) {
+            const rsrc_t r = make_rsrc(p.src[s] + b * kBlockBytes, n);
 #pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    v[u] ^= __builtin_nontemporal_load(p.src[s] + i);
-            }
+            for (int u = 0; u < kU; ++u)
+                buf.v[s][u] = load_vec(r, voff + u * kWave * kVecBytes);
         }
+    }
+
+    __device__ __forceinline__ void process(const Buf &buf, int64_t b) const
+    {
+        const uint32_t n = valid(b);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t i = b * per_block + u * kWave + lane;
-            if (i < n_vec) {
+        for (int d = 0; d < ND; ++d) {
+            const rsrc_t r = make_rsrc(p.dst[d] + b * kBlockBytes, n);
 #pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    __builtin_nontemporal_store(v[u], p.dst[d] + i);
+            for (int u = 0; u < kU; ++u) {
+                u32x4 v = buf.v[0][u];
+#pragma unroll
+                for (int s = 1; s < NS; ++s)
+                    v ^= buf.v[s][u];
+                store_vec(r, v, voff + u * kWave * kVecBytes);
             }
         }
     }
+};
+
+template <int NS, int ND>
+__global__ __launch_bounds__(kBlock) void stream_kernel(Ptrs p, int64_t n_vec)
+{
+    StreamOp<NS, ND> op{p, n_vec * kVecBytes, (uint32_t)lane_id() * kVecBytes};
+    walk_blocks(op, (n_vec * kVecBytes + kBlockBytes - 1) / kBlockBytes);
 }
 
 template <int NS, int ND>
@@ -65,7 +88,8 @@ int launch(const Ptrs &p, int64_t n_vec, int blocks, hipStream_t stream)
         hipDeviceProp_t prop;
         if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return 3;
-        blocks = prop.multiProcessorCount;
+        blocks = balanced_workgroups((n_vec * kVecBytes + kBlockBytes - 1) / kBlockBytes,
+                                     prop.multiProcessorCount, 1);
     }
     hipLaunchKernelGGL((stream_kernel<NS, ND>), dim3(blocks), dim3(kBlock), 0, stream, p, n_vec);
     return hipGetLastError() == hipSuccess ? 0 : 3;
@@ -87,12 +111,12 @@ extern "C" int hbm_probe_stream(const void *const *src, int n_src, void *const *
     for (int s = 0; s < n_src; ++s) {
         if (!src[s] || !aligned16(src[s]))
             return 1;
-        p.src[s] = static_cast<const u32x4 *>(src[s]);
+        p.src[s] = static_cast<const char *>(src[s]);
     }
     for (int d = 0; d < n_dst; ++d) {
         if (!dst[d] || !aligned16(dst[d]))
             return 1;
-        p.dst[d] = static_cast<u32x4 *>(dst[d]);
+        p.dst[d] = static_cast<char *>(dst[d]);
     }
     const uintptr_t bytes = (uintptr_t)n_vec * 16;
     for (int d = 0; d < n_dst; ++d)

@@ -88,6 +88,8 @@ moe_status_t moe_router_weight_bwd(const void *grad_out, moe_dtype_t out_dtype, 
  * Squared ReLU x routing probability, forward, bf16 in and out.
  *   clamp != 0: c = clamp_scale * tanh(x / clamp_scale); y = bf16(relu(c)^2 * p), all
  *               in fp32 with one final rounding; clamp_scale must be finite and > 0.
+ *               relu(c) is evaluated to 1.5e-6 relative (a rational form of tanh), so
+ *               y is within 1 bf16 ulp of the exactly rounded value.
  *   clamp == 0: y = bf16(bf16(relu(x)^2) * p): the square is rounded to bf16 first.
  *   x, y: [rows, hidden] bf16, hidden % 8 == 0; probs: fp32 [rows] indexed by slot.
  *   n_used, permutation_map, zero_padding: exactly as for swiglu_probs_fwd (device

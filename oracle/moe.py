@@ -9,6 +9,7 @@ file's header:
   ``router_weight_bwd``  NeMo AutoModel "moe/optimized_ops" page (_RouterWeightMulFunction)
 * ``squared_relu_probs`` Megatron-Core "core.inference.moe.batch_invariant" page
                          (_squared_relu_with_probs_kernel, squared_relu_with_probs)
+* ``squared_relu_probs_bwd`` the chain rule through that forward (the page gives none)
 * ``unpermute``          same page (_unpermute_tokens_in_expert_order_kernel)
 
 Element types are "bf16", "f16" or "f32"; 16-bit arrays are uint16 bit patterns.
@@ -57,10 +58,14 @@ class MoeOracle:
                                                  _vp, _vp, _i64, _i64]
         lib.oracle_squared_relu_probs_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int,
                                                       ctypes.c_float, _vp, _vp, ctypes.c_int]
+        lib.oracle_squared_relu_probs_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                                      ctypes.c_int, ctypes.c_float, _vp, _vp,
+                                                      ctypes.c_int]
         lib.oracle_unpermute_expert_order.argtypes = [_vp, _i64, _vp, _vp, _vp, ctypes.c_int, _i64,
                                                       _i64, _i64]
         for f in ("oracle_residual_add", "oracle_router_weight_fwd", "oracle_router_weight_bwd",
-                  "oracle_squared_relu_probs_fwd", "oracle_unpermute_expert_order"):
+                  "oracle_squared_relu_probs_fwd", "oracle_squared_relu_probs_bwd",
+                  "oracle_unpermute_expert_order"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
 
@@ -132,6 +137,35 @@ class MoeOracle:
                                                         _p(pm), int(bool(zero_padding))),
                  "oracle_squared_relu_probs_fwd")
         return y
+
+    def squared_relu_probs_bwd(self, x, probs, grad_y, *, clamp_scale=None, n_used=None,
+                               permutation_map=None, zero_padding=False, grad_x_out=None,
+                               grad_probs_out=None, want_grad_x=True):
+        """grad_x (bf16 bits), grad_probs (fp32, slot-indexed), grad_probs_f64 and the row
+        scale S = sum |g * y_pre| (both slot-indexed; NaN where a slot is not live)."""
+        x = _c(x, np.uint16)
+        g = _c(grad_y, np.uint16)
+        rows, hidden = x.shape
+        if g.shape != x.shape:
+            raise ValueError("shape mismatch")
+        probs = _c(np.asarray(probs).reshape(-1), np.float32)
+        gx = None
+        if want_grad_x:
+            gx = np.full((rows, hidden), 0xFFFF, np.uint16) if grad_x_out is None \
+                else _c(grad_x_out, np.uint16)
+        gp = np.full(rows, -12345.5, np.float32) if grad_probs_out is None \
+            else _c(grad_probs_out, np.float32)
+        gp64 = np.full(rows, np.nan)
+        sc = np.full(rows, np.nan)
+        nu = None if n_used is None else np.array([n_used], np.int32)
+        pm = None if permutation_map is None else _c(permutation_map, np.int32)
+        clamp = clamp_scale is not None
+        self._rc(self.lib.oracle_squared_relu_probs_bwd(_p(x), _p(probs), _p(g), _p(gx), _p(gp),
+                                                        _p(gp64), _p(sc), rows, hidden, int(clamp),
+                                                        float(clamp_scale or 0.0), _p(nu), _p(pm),
+                                                        int(bool(zero_padding))),
+                 "oracle_squared_relu_probs_bwd")
+        return {"grad_x": gx, "grad_probs": gp, "grad_probs_f64": gp64, "row_scale": sc}
 
     def unpermute(self, expert_output, inverse_map, out_dtype: str, *, valid_tokens=None, out=None):
         eo = _c(expert_output, np.uint16)

@@ -18,7 +18,9 @@
  *                     bf16 ReLU output is rounded to bf16 first, then multiplied by
  *                     the fp32 probability and rounded again. Rows follow the same
  *                     n_used / permutation_map / zero_padding rules as the SwiGLU
- *                     activation (see swiglu_oracle.c).
+ *                     activation (see swiglu_oracle.c). The backward, which the page
+ *                     does not give, is the chain rule through that forward (see
+ *                     oracle_squared_relu_probs_bwd).
  *   unpermute         same page, _unpermute_tokens_in_expert_order_kernel /
  *                     unpermute_tokens_in_expert_order: each output token sums its
  *                     local experts' contributions in fp32 in increasing expert id.
@@ -253,6 +255,84 @@ int oracle_squared_relu_probs_fwd(const uint16_t *x, const float *probs, uint16_
                 yr[h] = f32_to_bf16(sq * p);
             }
         }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Squared ReLU x probs, backward: the chain rule through the forward above.
+ * With y_pre the fp32 value the forward multiplies by p (a^2 with the soft clamp,
+ * the bf16-rounded square without it) and g = grad_y widened to fp32:
+ *   grad_x     = bf16( ((g * p) * (2 a)) * d )  where x > 0, else +0
+ *                d = dc/dx = sech^2(x / s) with the clamp, 1 without it
+ *   grad_probs = sum over the row of g * y_pre  (fp64 here, returned as fp32)
+ * The bf16 rounding of the square passes the gradient through unchanged, as a
+ * dtype cast does under autograd. The ReLU mask is x > 0 (for s > 0 the sign of
+ * s * tanh(x / s) is the sign of x), false for NaN, so a NaN input gets a zero
+ * gradient. sech^2 is written as 4 e / (1 + e)^2, e = e^(-2|z|): it equals
+ * 1 - tanh^2(z) but keeps its relative accuracy where tanh(z) rounds to 1.
+ * Rows follow the forward's rules; with zero_padding, grad_x of a row that is
+ * not live is +0; grad_probs is written only for live slots.
+ * ------------------------------------------------------------------------- */
+int oracle_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                  uint16_t *grad_x, float *grad_probs, double *grad_probs_f64,
+                                  double *row_scale, int64_t rows, int64_t hidden, int clamp,
+                                  float clamp_scale, const int32_t *n_used, const int32_t *perm,
+                                  int zero_padding)
+{
+    if (rows < 0 || hidden <= 0)
+        return 1;
+    if (clamp && !(clamp_scale > 0.0f && isfinite(clamp_scale)))
+        return 1;
+    int64_t bound = rows;
+    if (n_used) {
+        bound = *n_used < 0 ? 0 : *n_used;
+        if (bound > rows)
+            bound = rows;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t slot = -1;
+        if (r < bound) {
+            slot = perm ? (int64_t)perm[r] : r;
+            if (slot < 0 || slot >= rows)
+                slot = -1;
+        }
+        if (slot < 0) {
+            if (zero_padding && grad_x)
+                memset(grad_x + r * hidden, 0, (size_t)hidden * sizeof(uint16_t));
+            continue;
+        }
+        const float prob = probs[slot]; /* gathered through the map */
+        double acc = 0.0, scale = 0.0;
+        for (int64_t h = 0; h < hidden; ++h) {
+            const float v = bf16_to_f32(x[r * hidden + h]);
+            const float g = bf16_to_f32(grad_y[r * hidden + h]);
+            float ypre, gx;
+            if (clamp) {
+                float z = v / clamp_scale;
+                float c = clamp_scale * tanhf(z);
+                float a = (c < 0.0f) ? 0.0f : c; /* relu; NaN passes */
+                ypre = a * a;
+                float e = expf(-2.0f * fabsf(z));
+                float sech2 = (4.0f * e) / ((1.0f + e) * (1.0f + e));
+                gx = v > 0.0f ? ((g * prob) * (2.0f * a)) * sech2 : 0.0f;
+            } else {
+                float a = (v < 0.0f) ? 0.0f : v;
+                ypre = bf16_to_f32(f32_to_bf16(a * a));
+                gx = v > 0.0f ? (g * prob) * (2.0f * a) : 0.0f;
+            }
+            if (grad_x)
+                grad_x[r * hidden + h] = f32_to_bf16(gx);
+            const float term = g * ypre;
+            acc += (double)term;
+            scale += fabs((double)term);
+        }
+        if (grad_probs)
+            grad_probs[slot] = (float)acc;
+        if (grad_probs_f64)
+            grad_probs_f64[slot] = acc;
+        if (row_scale)
+            row_scale[slot] = scale;
     }
     return 0;
 }

@@ -12,6 +12,12 @@ Each ``pin_*`` takes a ``MoeOracle`` and raises ``AssertionError`` on disagreeme
                           bitwise), pin_squared_relu_clamp (torch fp64 reference within
                           1 ulp; large scale reduces to the unclamped fp32 square),
                           pin_squared_relu_rows (n_used / map / padding rules)
+* squared ReLU bwd     -> pin_squared_relu_bwd_fd (central differences of the fp64 forward
+                          for grad_x and grad_probs, out to tanh's saturation),
+                          pin_squared_relu_bwd_structure (s -> inf reduces to the unclamped
+                          gradient; linear in g; grad_probs free of p and equal to the
+                          forward's output at p = 1 without the clamp; masks and special
+                          values), pin_squared_relu_bwd_rows (n_used / map / padding)
 * unpermute            -> pin_unpermute (numpy float32 running sums in expert order;
                           single-contribution tokens copy the row exactly; bounds)
 """
@@ -195,6 +201,129 @@ def pin_squared_relu_rows(orc):
     assert np.all(y[[2, 9]] == 0) and np.array_equal(np.delete(y, [2, 9], 0), np.delete(full, [2, 9], 0))
 
 
+def _bf16_values(rng, shape, scale, min_abs):
+    """bf16 bit patterns ~ N(0, scale^2) kept at least min_abs away from 0 (the kink)."""
+    v = rng.standard_normal(shape) * scale
+    v = np.where(np.abs(v) < min_abs, np.copysign(min_abs, v) + v, v).astype(np.float32)
+    return _torch_to_np(torch.from_numpy(v), "bf16")
+
+
+def _sqrelu_fwd64(xd, pd, s, round_square):
+    """The page's forward in fp64 (no final rounding). Without the clamp the square of
+    the bf16 ReLU output is rounded to bf16 when round_square is set."""
+    if s is None:
+        sq = np.maximum(xd, 0.0) ** 2
+        if round_square:
+            sq = bf16_bits_to_f32(_torch_to_np(torch.from_numpy(sq.astype(np.float32)), "bf16")).astype(np.float64)
+        return sq * pd
+    return np.maximum(s * np.tanh(xd / s), 0.0) ** 2 * pd
+
+
+def pin_squared_relu_bwd_fd(orc):
+    """grad_x = g * dy/dx and grad_probs = sum g * dy/dp by central differences in fp64.
+    Past |x / s| = 5 a difference of the saturated forward is rounding noise, so there
+    dy/dx comes from the textbook derivative of tanh, 1 / cosh^2, in fp64 (accurate to
+    |z| ~ 700). With s = 0.7, |x / s| reaches ~25: sech^2 down to 1e-21, where
+    1 - tanh^2 from an fp32 tanh has no digits left."""
+    rng = np.random.default_rng(11)
+    rows, hidden = 8, 64
+    x = _bf16_values(rng, (rows, hidden), 4.0, 1e-2)
+    g = _torch_to_np(torch.from_numpy(rng.standard_normal((rows, hidden)).astype(np.float32)), "bf16")
+    p = rng.uniform(0.1, 1.0, rows).astype(np.float32)
+    xd = bf16_bits_to_f32(x).astype(np.float64)
+    gd = bf16_bits_to_f32(g).astype(np.float64)
+    pd = p.astype(np.float64)[:, None]
+    for s in (None, 0.7, 4.0):
+        o = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=s)
+        h = 1e-6 * np.maximum(1.0, np.abs(xd))
+        dydx = (_sqrelu_fwd64(xd + h, pd, s, False) - _sqrelu_fwd64(xd - h, pd, s, False)) / (2 * h)
+        if s is not None:
+            z = xd / s
+            far = np.abs(z) > 5.0
+            assert s > 1.0 or far.sum() > 20, "the small scale must reach deep saturation"
+            exact = 2.0 * np.maximum(s * np.tanh(z), 0.0) / np.cosh(z) ** 2 * pd
+            dydx = np.where(far, exact, dydx)
+        want = _torch_to_np(torch.from_numpy((gd * dydx).astype(np.float32)), "bf16")
+        assert_within_ulp(o["grad_x"], want, 1, f"squared relu grad_x by differences, s={s}")
+        hp = 1e-6
+        lp = (gd * _sqrelu_fwd64(xd, pd + hp, s, True)).sum(1)
+        lm = (gd * _sqrelu_fwd64(xd, pd - hp, s, True)).sum(1)
+        fd = (lp - lm) / (2 * hp)
+        bad = grad_probs_violations(o["grad_probs"], fd, o["row_scale"])
+        assert bad.size == 0, f"squared relu grad_probs by differences, s={s}"
+        assert np.all(np.abs(o["grad_probs_f64"] - fd) <= 1e-6 * o["row_scale"] + 1e-9)  # fp32 terms
+
+
+def pin_squared_relu_bwd_structure(orc):
+    rng = np.random.default_rng(12)
+    rows, hidden = 16, 96
+    x = _bf16_values(rng, (rows, hidden), 3.0, 1e-3)
+    g = _torch_to_np(torch.from_numpy(rng.standard_normal((rows, hidden)).astype(np.float32)), "bf16")
+    p = rng.uniform(0.05, 1.0, rows).astype(np.float32)
+    plain = orc.squared_relu_probs_bwd(x, p, g)
+    # a huge scale makes the soft clamp the identity: the unclamped gradient
+    big = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=1e30)
+    assert_within_ulp(big["grad_x"], plain["grad_x"], 1, "s -> inf")
+    assert np.array_equal(plain["grad_x"][bf16_bits_to_f32(x) <= 0], np.zeros((bf16_bits_to_f32(x) <= 0).sum(), np.uint16))
+    for s in (None, 2.0):
+        o = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=s)
+        # linear in g: doubling grad_y (exact in bf16) doubles grad_x exactly
+        g2 = _torch_to_np(_np_to_torch(g, "bf16").float() * 2, "bf16")
+        o2 = orc.squared_relu_probs_bwd(x, p, g2, clamp_scale=s)
+        a, b = bf16_bits_to_f32(o["grad_x"]), bf16_bits_to_f32(o2["grad_x"])
+        ok = np.abs(a) > 1e-30
+        assert np.array_equal(b[ok], 2 * a[ok]), f"linear in g, s={s}"
+        # grad_probs does not depend on p; grad_x vanishes with p
+        o3 = orc.squared_relu_probs_bwd(x, np.zeros_like(p), g, clamp_scale=s)
+        assert np.array_equal(o3["grad_probs"], o["grad_probs"]), f"grad_probs free of p, s={s}"
+        assert np.all(bf16_bits_to_f32(o3["grad_x"]) == 0)
+    # without the clamp, y_pre is the forward's output at p = 1 (the bf16 square)
+    y1 = bf16_bits_to_f32(orc.squared_relu_probs(x, np.ones(rows, np.float32))).astype(np.float64)
+    want = (bf16_bits_to_f32(g).astype(np.float32) * y1.astype(np.float32)).astype(np.float64).sum(1)
+    assert np.all(np.abs(plain["grad_probs_f64"] - want) <= 1e-12 * plain["row_scale"]), "y_pre is the bf16 square"
+    # masks and special values: x <= 0, -0, -inf and NaN give +0; +inf saturates the clamp
+    sp = np.array([0x0000, 0x8000, 0xFF80, 0x7FC0, 0xC040, 0x7F80, 0x3F80, 0x0001], np.uint16)
+    xs = np.tile(sp, (2, 1))
+    gs = np.full_like(xs, 0xBF80)                                  # grad_y = -1
+    ps = np.array([0.5, 0.25], np.float32)
+    for s in (None, 1.5):
+        o = orc.squared_relu_probs_bwd(xs, ps, gs, clamp_scale=s)
+        assert np.all(o["grad_x"][:, :5] == 0x0000), f"mask gives +0, s={s}"
+        if s is None:
+            assert np.all(o["grad_x"][:, 5] == 0xFF80), "(g p) (2 inf) = -inf"
+        else:
+            assert np.all(o["grad_x"][:, 5] == 0x8000), "sech^2(inf) = 0: -0"
+        assert np.all(bf16_bits_to_f32(o["grad_x"][:, 6]) < 0)
+        assert np.all(np.isnan(o["grad_probs"])), "the row holds a NaN input"
+
+
+def pin_squared_relu_bwd_rows(orc):
+    rng = np.random.default_rng(13)
+    rows, hidden = 40, 64
+    x = _bf16_values(rng, (rows, hidden), 3.0, 1e-3)
+    g = _torch_to_np(torch.from_numpy(rng.standard_normal((rows, hidden)).astype(np.float32)), "bf16")
+    p = rng.uniform(0, 1, rows).astype(np.float32)
+    full = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=2.0)
+    perm = rng.permutation(rows).astype(np.int32)
+    pm = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=2.0, permutation_map=perm)
+    ref = orc.squared_relu_probs_bwd(x, p[perm], g, clamp_scale=2.0)
+    assert np.array_equal(pm["grad_x"], ref["grad_x"]), "p gathered through the map"
+    assert np.array_equal(pm["grad_probs"][perm], ref["grad_probs"]), "grad_probs scattered to the slot"
+    for k in (0, 13, rows):
+        for zp in (False, True):
+            o = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=2.0, n_used=k, zero_padding=zp)
+            assert np.array_equal(o["grad_x"][:k], full["grad_x"][:k])
+            assert np.all(o["grad_x"][k:] == (0 if zp else 0xFFFF))
+            assert np.array_equal(o["grad_probs"][:k], full["grad_probs"][:k])
+            assert np.all(o["grad_probs"][k:] == -12345.5), "slots that are not live stay untouched"
+    m = np.arange(rows, dtype=np.int32)
+    m[[2, 9]] = [-1, rows]
+    o = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=2.0, permutation_map=m, zero_padding=True)
+    assert np.all(o["grad_x"][[2, 9]] == 0)
+    assert np.array_equal(np.delete(o["grad_x"], [2, 9], 0), np.delete(full["grad_x"], [2, 9], 0))
+    assert np.all(o["grad_probs"][[2, 9]] == -12345.5)
+
+
 def pin_unpermute(orc):
     rng = np.random.default_rng(7)
     tokens, E, hidden, erows = 50, 6, 48, 120
@@ -237,4 +366,6 @@ def pin_unpermute(orc):
 
 
 ALL_PINS = [pin_f16_conversions, pin_residual_add, pin_router_weight_fwd, pin_router_weight_bwd,
-            pin_squared_relu_no_clamp, pin_squared_relu_clamp, pin_squared_relu_rows, pin_unpermute]
+            pin_squared_relu_no_clamp, pin_squared_relu_clamp, pin_squared_relu_rows,
+            pin_squared_relu_bwd_fd, pin_squared_relu_bwd_structure, pin_squared_relu_bwd_rows,
+            pin_unpermute]

@@ -27,6 +27,19 @@ MUTANTS = [
     ("sqrelu_scale_inverted", "tanhf(v / clamp_scale)", "tanhf(v * clamp_scale)"),
     ("sqrelu_no_relu", "float a = c < 0.0f ? 0.0f : c;", "float a = c;"),
     ("sqrelu_map_not_gathered", "const float p = probs[slot];", "const float p = probs[r];"),
+    ("sqrelu_bwd_no_factor_two", "((g * prob) * (2.0f * a)) * sech2", "((g * prob) * a) * sech2"),
+    ("sqrelu_bwd_sech2_from_fp32_tanh", "float sech2 = (4.0f * e) / ((1.0f + e) * (1.0f + e));",
+     "float sech2 = 1.0f - tanhf(z) * tanhf(z);"),
+    ("sqrelu_bwd_sech_not_squared", "float sech2 = (4.0f * e) / ((1.0f + e) * (1.0f + e));",
+     "float sech2 = (4.0f * e) / (1.0f + e);"),
+    ("sqrelu_bwd_mask_includes_zero", "gx = v > 0.0f ? ((g * prob)", "gx = v >= 0.0f ? ((g * prob)"),
+    ("sqrelu_bwd_nan_passes_mask", "gx = v > 0.0f ? (g * prob) * (2.0f * a) : 0.0f;",
+     "gx = !(v <= 0.0f) ? (g * prob) * (2.0f * a) : 0.0f;"),
+    ("sqrelu_bwd_no_relu", "float a = (c < 0.0f) ? 0.0f : c; /* relu; NaN passes */", "float a = c;"),
+    ("sqrelu_bwd_grad_probs_times_p", "const float term = g * ypre;", "const float term = g * ypre * prob;"),
+    ("sqrelu_bwd_square_not_rounded", "ypre = bf16_to_f32(f32_to_bf16(a * a));", "ypre = a * a;"),
+    ("sqrelu_bwd_no_gather", "const float prob = probs[slot];", "const float prob = probs[r];"),
+    ("sqrelu_bwd_padding_not_zeroed", "if (zero_padding && grad_x)", "if (0 && grad_x)"),
     ("unpermute_reversed", "for (int64_t e = 0; e < num_local_experts; ++e) {",
      "for (int64_t e = num_local_experts - 1; e >= 0; --e) {"),
     ("unpermute_bound_off_by_one", "for (int64_t t = 0; t < bound; ++t)", "for (int64_t t = 0; t < bound + (bound < tokens); ++t)"),

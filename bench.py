@@ -158,11 +158,14 @@ def bench_moe(args) -> int:
         nbytes = {"fwd": moe_algorithmic_bytes(op, inp, "fwd"), "bwd": moe_algorithmic_bytes(op, inp, "bwd")}
         shape = {"rows": x.shape[0], "hidden": x.shape[1]}
     elif op == "squared_relu":
-        x = bits(inp["x"])
+        x, gy = bits(inp["x"]), bits(inp["grad_y"])
         p = torch.from_numpy(inp["probs"]).to(dev)
-        y = torch.empty_like(x)
-        kernels = [("squared_relu", lambda: mbe.moe_squared_relu_probs_fwd(x, p, y, clamp_scale=inp["clamp_scale"]))]
-        nbytes = {"squared_relu": moe_algorithmic_bytes(op, inp)}
+        y, gx = torch.empty_like(x), torch.empty_like(x)
+        gp = torch.empty_like(p)
+        s = inp["clamp_scale"]
+        kernels = [("fwd", lambda: mbe.moe_squared_relu_probs_fwd(x, p, y, clamp_scale=s)),
+                   ("bwd", lambda: mbe.moe_squared_relu_probs_bwd(x, p, gy, gx, gp, clamp_scale=s))]
+        nbytes = {"fwd": moe_algorithmic_bytes(op, inp, "fwd"), "bwd": moe_algorithmic_bytes(op, inp, "bwd")}
         shape = {"rows": x.shape[0], "hidden": x.shape[1], "clamp_scale": inp["clamp_scale"]}
     else:
         eo = bits(inp["expert_output"])
@@ -210,6 +213,8 @@ def bench_moe(args) -> int:
             elif op == "squared_relu":
                 n = int(inp["x"].shape[0] * frac)
                 orc.squared_relu_probs(inp["x"][:n], inp["probs"][:n], clamp_scale=inp["clamp_scale"])
+                orc.squared_relu_probs_bwd(inp["x"][:n], inp["probs"][:n], inp["grad_y"][:n],
+                                           clamp_scale=inp["clamp_scale"])
                 moved += int(total * n / inp["x"].shape[0])
             else:
                 n = int(inp["inverse_map"].shape[0] * frac)

@@ -102,6 +102,34 @@ moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, u
                                         hipStream_t stream, int num_workgroups);
 
 /*
+ * Squared ReLU x routing probability, backward: the chain rule through the forward
+ * above (Megatron-Core "core.inference.moe.batch_invariant" page gives the forward
+ * only). With g = grad_y, y_pre the fp32 value the forward multiplies by p (relu(c)^2
+ * with the clamp, the bf16-rounded square without it) and a = relu(c) (c = x without
+ * the clamp):
+ *   grad_x[r, j]     = bf16(((g * p) * (2 a)) * d) where x > 0, else +0 (also for NaN),
+ *                      d = sech^2(x / clamp_scale) with the clamp, 1 without it; the
+ *                      bf16 rounding of the square passes the gradient through.
+ *   grad_probs[slot] = sum over j of g * y_pre, in fp32 in a fixed order that does not
+ *                      depend on the grid.
+ *   x, grad_y, grad_x: [rows, hidden] bf16, 16-byte aligned, hidden % 8 == 0.
+ *   probs: fp32 [rows] indexed by slot; grad_probs: fp32 [rows] or NULL (skip).
+ *   n_used, permutation_map, zero_padding: as for the forward. Rows that are not live
+ *   read nothing; their grad_x is +0 with zero_padding and untouched without it; their
+ *   grad_probs slots are never written.
+ *   The clamp path is within 1 bf16 ulp of the exactly rounded gradient (its tanh and
+ *   sech^2 are evaluated to about 1e-6 relative); the unclamped grad_x is the fp32
+ *   expression above, rounded once.
+ *   Errors: INVALID_ARG (null x / probs / grad_y / grad_x, rows < 0, hidden <= 0, a bad
+ *   clamp_scale, an output overlapping an input or the other output), ALIGNMENT.
+ */
+moe_status_t moe_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                        uint16_t *grad_x, float *grad_probs, int64_t rows,
+                                        int64_t hidden, int clamp, float clamp_scale,
+                                        const int32_t *n_used, const int32_t *permutation_map,
+                                        int zero_padding, hipStream_t stream, int num_workgroups);
+
+/*
  * out[t, :] = sum over e = 0, 1, ..., num_local_experts-1 with 0 <= inverse_map[t, e] <
  *             expert_rows of expert_output[inverse_map[t, e], :], accumulated in fp32 in
  *             that order from +0; stored as fp32 or rounded once to bf16 (out_dtype).

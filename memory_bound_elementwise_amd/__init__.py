@@ -5,7 +5,7 @@ behind the C ABI of ``include/swiglu_probs.h``; this package holds the kernels'
 sources (``csrc/``), their in-tree build (``build.py``), the ctypes binding
 (``swiglu_probs``), the binding of the MoE elementwise operations next to the
 activation (``moe_elementwise``: fused residual add, router-weight multiply,
-squared-ReLU x probs, unpermute in expert order), the HBM probe binding
+squared-ReLU x probs forward and backward, unpermute in expert order), the HBM probe binding
 (``hbm_probe``) and the seeded input generators (``workloads``). Libraries are
 loaded on first use, not at import.
 """
@@ -14,12 +14,13 @@ from .swiglu_probs import (SwigluProbs, SwigluProbsError, backward, forward,  # 
                            swiglu_probs_fwd)
 
 from .moe_elementwise import (FusedMoEResidualAdd, MoeElementwiseError,  # noqa: F401
-                              RouterWeightMul, moe_residual_add, moe_router_weight_bwd,
-                              moe_router_weight_fwd, moe_squared_relu_probs_fwd,
+                              RouterWeightMul, SquaredReluProbs, moe_residual_add,
+                              moe_router_weight_bwd, moe_router_weight_fwd,
+                              moe_squared_relu_probs_bwd, moe_squared_relu_probs_fwd,
                               moe_unpermute_expert_order)
 
 __all__ = ["moe_residual_add", "moe_router_weight_fwd", "moe_router_weight_bwd",
-           "moe_squared_relu_probs_fwd", "moe_unpermute_expert_order", "FusedMoEResidualAdd",
-           "RouterWeightMul", "MoeElementwiseError",
+           "moe_squared_relu_probs_fwd", "moe_squared_relu_probs_bwd", "moe_unpermute_expert_order",
+           "FusedMoEResidualAdd", "RouterWeightMul", "SquaredReluProbs", "MoeElementwiseError",
            "swiglu_probs_fwd", "swiglu_probs_bwd", "swiglu_probs_default_workgroups",
            "forward", "backward", "SwigluProbs", "SwigluProbsError", "load_library"]

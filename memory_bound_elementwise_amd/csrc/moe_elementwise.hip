@@ -420,6 +420,119 @@ __global__ __launch_bounds__(kBlock) void squared_relu_probs_kernel(
     walk_rows(op, sched, perm, probs, nch);
 }
 
+// Squared ReLU x probs, backward: grad_x = ((g p) (2a)) d where x > 0, else +0, with
+// d = sech^2(x / s) under the soft clamp and 1 without it, and the row sum of
+// g * y_pre (y_pre = a^2, or the bf16-rounded square without the clamp) as the
+// probability gradient.
+//
+// Under the clamp, E = e^(-2z) and r = 1 / (1 + E) give both factors with two
+// quarter-rate operations: tanh z = (1 - E) r (for z >= 1/8; below, the odd series
+// z - z^3/3 + 2z^5/15, whose first omitted term is under 2.2e-7 of z there) and
+// sech^2 z = 4 E r^2, which stays accurate where tanh rounds to 1. The ReLU is taken
+// first (z = max(x / s, 0), NaN kept), so only z >= 0 is ever evaluated.
+template <int U, bool kClamp>
+struct SquaredReluBwdOp {
+    struct Buf {
+        u32x4 x[U], g[U];
+    };
+    const uint16_t *x;
+    const uint16_t *g;
+    uint16_t *gx;
+    float *gp;
+    int hidden;
+    int nch;
+    float s, inv_s;
+    int zero_padding;
+    uint32_t voff;
+    float acc;  // this lane's partial of the current row's probability gradient
+
+    __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
+    {
+        const uint32_t row = (uint32_t)hidden * 2u, off = (uint32_t)c * U * kWave * kVecBytes;
+        const rsrc_t rx = chunk_rsrc(x + r * hidden, live ? row : 0u, off);
+        const rsrc_t rg = chunk_rsrc(g + r * hidden, live ? row : 0u, off);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            b.x[u] = load_vec(rx, voff + u * kWave * kVecBytes);
+            b.g[u] = load_vec(rg, voff + u * kWave * kVecBytes);
+        }
+    }
+
+    // two elements (one packed word of x and of g): the packed bf16 gradients; the
+    // terms g * y_pre go into acc in element order
+    __device__ __forceinline__ unsigned pair(unsigned xw, unsigned gw, float p)
+    {
+        const float v[2] = {bf16_lo(xw), bf16_hi(xw)}, gv[2] = {bf16_lo(gw), bf16_hi(gw)};
+        float grad[2], ypre[2];
+        if constexpr (kClamp) {
+            constexpr float kNeg2Log2e = -2.8853900817779268f;
+            constexpr float kThird = -1.0f / 3.0f, kTwoFifteenths = 2.0f / 15.0f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float z = __builtin_elementwise_maximum(v[i] * inv_s, 0.0f);
+                // v_exp_f32 flushes subnormal results: e^(-2z) * 2^64 is formed instead
+                // and scaled back by a multiply, which keeps e (and so sech^2) down to
+                // the smallest subnormal, as the fp32 chain has it
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z, kNeg2Log2e, 64.0f)) * 0x1p-64f;
+                const float r = __builtin_amdgcn_rcpf(1.0f + e);
+                const float u = z * z;
+                const float small = z * __builtin_fmaf(u, __builtin_fmaf(u, kTwoFifteenths, kThird), 1.0f);
+                const float t = z < 0.125f ? small : (1.0f - e) * r;
+                const float a = s * t;
+                const float sech2 = ((4.0f * e) * r) * r;
+                ypre[i] = a * a;
+                grad[i] = ((gv[i] * p) * (2.0f * a)) * sech2;
+            }
+        } else {
+            const float a[2] = {__builtin_elementwise_maximum(v[0], 0.0f),
+                                __builtin_elementwise_maximum(v[1], 0.0f)};
+            const unsigned sq = pack_bf16x2(a[0] * a[0], a[1] * a[1]);  // the square in bf16
+            ypre[0] = bf16_lo(sq);
+            ypre[1] = bf16_hi(sq);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                grad[i] = (gv[i] * p) * (2.0f * a[i]);
+        }
+        acc += gv[0] * ypre[0];
+        acc += gv[1] * ypre[1];
+        return pack_bf16x2(v[0] > 0.0f ? grad[0] : 0.0f, v[1] > 0.0f ? grad[1] : 0.0f);
+    }
+
+    __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p)
+    {
+        const uint32_t row = (uint32_t)hidden * 2u;
+        const rsrc_t rgx = chunk_rsrc(gx + r * hidden, (slot >= 0 || zero_padding) ? row : 0u,
+                                      (uint32_t)c * U * kWave * kVecBytes);
+        if (c == 0)
+            acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pair(b.x[u][q], b.g[u][q], p);
+            store_vec(rgx, o, voff + u * kWave * kVecBytes);
+        }
+        if (c == nch - 1 && slot >= 0 && gp) {
+            const float total = wave_sum(acc);
+            if (lane_id() == 0)
+                gp[slot] = total;
+        }
+    }
+};
+
+template <int U, bool kClamp>
+__global__ __launch_bounds__(kBlock) void squared_relu_probs_bwd_kernel(
+    const uint16_t *x, const float *probs, const uint16_t *g, uint16_t *gx, float *gp, int rows,
+    int hidden, float s, float inv_s, const int *n_used, const int *perm, int zero_padding)
+{
+    const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
+    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
+    SquaredReluBwdOp<U, kClamp> op{x, g, gx, gp, hidden, nch, s, inv_s, zero_padding,
+                                   (uint32_t)lane_id() * kVecBytes, 0.0f};
+    walk_rows(op, sched, perm, probs, nch);
+}
+
 // ---------------------------------------------------------------------------
 // Token-local unpermute in fixed expert order
 // ---------------------------------------------------------------------------
@@ -624,6 +737,28 @@ void launch_sqrelu(int U, int blocks, hipStream_t st, const uint16_t *x, const f
     }
 }
 
+template <int U, bool C>
+void launch_sqrelu_bwd_u(int blocks, hipStream_t st, const uint16_t *x, const float *p, const uint16_t *g,
+                         uint16_t *gx, float *gp, int rows, int hidden, float s, float inv_s, const int *nu,
+                         const int *pm, int zp)
+{
+    hipLaunchKernelGGL((squared_relu_probs_bwd_kernel<U, C>), dim3(blocks), dim3(kBlock), 0, st, x, p, g,
+                       gx, gp, rows, hidden, s, inv_s, nu, pm, zp);
+}
+
+template <bool C>
+void launch_sqrelu_bwd(int U, int blocks, hipStream_t st, const uint16_t *x, const float *p,
+                       const uint16_t *g, uint16_t *gx, float *gp, int rows, int hidden, float s,
+                       float inv_s, const int *nu, const int *pm, int zp)
+{
+    switch (U) {
+    case 1: launch_sqrelu_bwd_u<1, C>(blocks, st, x, p, g, gx, gp, rows, hidden, s, inv_s, nu, pm, zp); break;
+    case 2: launch_sqrelu_bwd_u<2, C>(blocks, st, x, p, g, gx, gp, rows, hidden, s, inv_s, nu, pm, zp); break;
+    case 3: launch_sqrelu_bwd_u<3, C>(blocks, st, x, p, g, gx, gp, rows, hidden, s, inv_s, nu, pm, zp); break;
+    default: launch_sqrelu_bwd_u<4, C>(blocks, st, x, p, g, gx, gp, rows, hidden, s, inv_s, nu, pm, zp); break;
+    }
+}
+
 // unpermute: G experts per batch of loads, U octs per lane per chunk
 #ifndef MOE_UNPERMUTE_U
 #define MOE_UNPERMUTE_U 4
@@ -802,6 +937,52 @@ moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, u
     else
         launch_sqrelu<false>(U, blocks, stream, x, probs, y, (int)rows, (int)hidden, s, 1.0f, n_used,
                              permutation_map, zero_padding ? 1 : 0);
+    return launched();
+}
+
+moe_status_t moe_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                        uint16_t *grad_x, float *grad_probs, int64_t rows,
+                                        int64_t hidden, int clamp, float clamp_scale,
+                                        const int32_t *n_used, const int32_t *permutation_map,
+                                        int zero_padding, hipStream_t stream, int num_workgroups)
+{
+    if (rows < 0 || hidden <= 0 || rows > kMaxRows || hidden > kMaxHidden || num_workgroups < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (clamp && !(clamp_scale > 0.0f && std::isfinite(clamp_scale)))
+        return MOE_ERR_INVALID_ARG;
+    if (hidden % 8 != 0)
+        return MOE_ERR_ALIGNMENT;
+    if (rows == 0)
+        return MOE_OK;
+    if (!x || !probs || !grad_y || !grad_x)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(grad_y, 16) || !aligned(grad_x, 16) || !aligned(probs, 4) ||
+        !aligned(grad_probs, 4) || !aligned(n_used, 4) || !aligned(permutation_map, 4))
+        return MOE_ERR_ALIGNMENT;
+    const uint64_t R = (uint64_t)rows, H = (uint64_t)hidden;
+    const Range outs[] = {span(grad_x, R * H * 2), span(grad_probs, R * 4)};
+    const Range ins[] = {span(x, R * H * 2), span(grad_y, R * H * 2), span(probs, R * 4), span(n_used, 4),
+                         span(permutation_map, R * 4)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i))
+                return MOE_ERR_INVALID_ARG;
+    if (overlap(outs[0], outs[1]))
+        return MOE_ERR_INVALID_ARG;
+    int cus = 0;
+    hipError_t he = device_cus(&cus);
+    if (he != hipSuccess)
+        return fail_hip(he);
+    const int U = pick_u(hidden / 8);
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : balanced_workgroups(rows, cus * kSquaredReluBlocksPerCU, 1);
+    const float s = clamp ? clamp_scale : 1.0f;
+    if (clamp)
+        launch_sqrelu_bwd<true>(U, blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows,
+                                (int)hidden, s, 1.0f / s, n_used, permutation_map, zero_padding ? 1 : 0);
+    else
+        launch_sqrelu_bwd<false>(U, blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows,
+                                 (int)hidden, s, 1.0f, n_used, permutation_map, zero_padding ? 1 : 0);
     return launched();
 }
 

@@ -31,6 +31,8 @@ _SIGS = {
     "moe_router_weight_bwd": [_vp, _int, _vp, _int, _vp, _vp, _vp, _i64, _i64, _vp, _int],
     "moe_squared_relu_probs_fwd": [_vp, _vp, _vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp, _int,
                                    _vp, _int],
+    "moe_squared_relu_probs_bwd": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp,
+                                   _int, _vp, _int],
     "moe_unpermute_expert_order": [_vp, _i64, _vp, _vp, _vp, _int, _i64, _i64, _int, _vp, _int],
     "moe_elementwise_status_string": [_int],
     "moe_elementwise_last_hip_error": [],
@@ -185,6 +187,35 @@ def moe_squared_relu_probs_fwd(x, probs, y, *, clamp_scale=None, n_used=None, pe
     return y
 
 
+def moe_squared_relu_probs_bwd(x, probs, grad_y, grad_x, grad_probs=None, *, clamp_scale=None,
+                               n_used=None, permutation_map=None, zero_padding=False, stream=None,
+                               num_workgroups=0):
+    """Backward of ``moe_squared_relu_probs_fwd``: grad_x (bf16) and, when given, grad_probs
+    (fp32 [rows], indexed by slot; slots of rows that are not live are left as they are)."""
+    if x.dim() != 2 or x.element_size() != 2 or grad_y.shape != x.shape or grad_x.shape != x.shape \
+            or grad_y.element_size() != 2 or grad_x.element_size() != 2:
+        raise ValueError("x, grad_y and grad_x must be bf16 [rows, hidden]")
+    rows, hidden = x.shape
+    if probs.dtype != torch.float32 or probs.numel() != rows:
+        raise ValueError("probs must be fp32 with one value per row")
+    if grad_probs is not None and (grad_probs.dtype != torch.float32 or grad_probs.numel() != rows):
+        raise ValueError("grad_probs must be fp32 with one value per row")
+    if n_used is not None and (n_used.dtype != torch.int32 or n_used.numel() != 1):
+        raise ValueError("n_used must be a device int32 scalar")
+    if permutation_map is not None and (permutation_map.dtype != torch.int32 or
+                                        permutation_map.numel() != rows):
+        raise ValueError("permutation_map must be int32 [rows]")
+    dev = _dev(x, probs, grad_y, grad_x, grad_probs, n_used, permutation_map)
+    clamp = clamp_scale is not None
+    st = load_library().moe_squared_relu_probs_bwd(_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x),
+                                                   _ptr(grad_probs), rows, hidden, int(clamp),
+                                                   float(clamp_scale if clamp else 0.0), _ptr(n_used),
+                                                   _ptr(permutation_map), int(bool(zero_padding)),
+                                                   _stream(stream, dev), int(num_workgroups))
+    _check("moe_squared_relu_probs_bwd", st)
+    return grad_x, grad_probs
+
+
 def moe_unpermute_expert_order(expert_output, inverse_map, out, *, valid_tokens=None,
                                out_dtype=None, stream=None, num_workgroups=0):
     """out[t] = sum over local experts e in increasing order of expert_output[inverse_map[t, e]]."""
@@ -244,3 +275,26 @@ class RouterWeightMul(torch.autograd.Function):
                               x_dtype={torch.bfloat16: "bf16", torch.float16: "f16",
                                        torch.float32: "f32"}[ctx.x_dtype])
         return gx, gp, None
+
+
+class SquaredReluProbs(torch.autograd.Function):
+    """relu(x)^2 * probs, or relu(s * tanh(x / s))^2 * probs with ``clamp_scale`` s, in the
+    HIP kernels. Saves only ``x`` and ``probs``; the backward recomputes the activation.
+    ``x`` bf16 [rows, hidden] contiguous, ``probs`` fp32 [rows] or [rows, 1]; every row live."""
+
+    @staticmethod
+    def forward(ctx, x, probs, clamp_scale=None):
+        ctx.save_for_backward(x, probs)
+        ctx.clamp_scale = clamp_scale
+        return moe_squared_relu_probs_fwd(x, probs.reshape(-1), torch.empty_like(x),
+                                          clamp_scale=clamp_scale)
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        x, probs = ctx.saved_tensors
+        gx = torch.empty_like(x)
+        gp = torch.empty(probs.numel(), dtype=torch.float32, device=x.device) \
+            if ctx.needs_input_grad[1] else None
+        moe_squared_relu_probs_bwd(x, probs.reshape(-1), grad_y.contiguous(), gx, gp,
+                                   clamp_scale=ctx.clamp_scale)
+        return gx, (None if gp is None else gp.view(probs.shape)), None

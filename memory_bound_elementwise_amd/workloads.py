@@ -179,7 +179,8 @@ def make_moe_inputs(op: str, seed: int = 0, scale: float = 1.0) -> dict:
 
     residual_add : expert, shared, residual bf16 [6720, 7168] ~ N(0,1) (residual N(0, 4^2))
     router_weight: x bf16 [53760, 7168] ~ N(0,1), probs U(0,1), grad_out bf16 ~ N(0,1)
-    squared_relu : x bf16 [53760, 2048] ~ N(0, 3^2), probs U(0,1), soft clamp scale 4
+    squared_relu : x bf16 [53760, 2048] ~ N(0, 3^2), probs U(0,1), soft clamp scale 4,
+                   grad_y bf16 [53760, 2048] ~ N(0, 1) for the backward
     unpermute    : 6720 tokens x 8 local experts, each (token, expert) pair routed with
                    probability 1/2; expert_output bf16 [routed pairs, 7168] ~ N(0,1) in
                    expert-major (grouped-GEMM) order; inverse_map int32 [6720, 8]
@@ -204,7 +205,7 @@ def make_moe_inputs(op: str, seed: int = 0, scale: float = 1.0) -> dict:
     if op == "squared_relu":
         x = bf16((rows, 2048), 3.0)
         probs = torch.rand(rows, generator=g, dtype=torch.float32).numpy()
-        return {"x": x, "probs": probs, "clamp_scale": 4.0}
+        return {"x": x, "probs": probs, "clamp_scale": 4.0, "grad_y": bf16((rows, 2048))}
     if op == "unpermute":
         valid = (torch.rand(tokens, MOE_LOCAL_EXPERTS, generator=g) < 0.5).numpy()
         im = np.full((tokens, MOE_LOCAL_EXPERTS), -1, np.int32)
@@ -228,7 +229,9 @@ def moe_algorithmic_bytes(op: str, inp: dict, direction: str = "fwd") -> int:
         return n * 2 * 3 + rows * 8                          # read g and x, write grad_x; probs, grad_probs
     if op == "squared_relu":
         n, rows = inp["x"].size, inp["x"].shape[0]
-        return n * 2 * 2 + rows * 4
+        if direction == "fwd":
+            return n * 2 * 2 + rows * 4                      # read x, write y; probs
+        return n * 2 * 3 + rows * 8                          # read x and grad_y, write grad_x; probs, grad_probs
     if op == "unpermute":
         im = inp["inverse_map"]
         contrib = int((im >= 0).sum())

@@ -166,6 +166,20 @@ def test_moe_validation():
     assert sq(a, b, c, 4, 8, 1, float("nan"), None, None, 0, None, 0) == 1
     assert sq(a, b, c, 0, 8, 0, 0.0, None, None, 0, None, 0) == 0
     assert sq(a, b, a, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1
+    sb = lib.moe_squared_relu_probs_bwd
+    e = A16 + (4 << 24)
+    assert sb(a, b, c, d, e, 0, 8, 1, 2.0, None, None, 0, None, 0) == 0   # empty: no launch
+    assert sb(a, b, c, d, e, 4, 8, 1, -2.0, None, None, 0, None, 0) == 1  # clamp needs scale > 0
+    assert sb(a, b, c, d, e, 4, 12, 0, 0.0, None, None, 0, None, 0) == 2  # hidden % 8
+    assert sb(a, b, c + 8, d, e, 4, 8, 0, 0.0, None, None, 0, None, 0) == 2   # grad_y alignment
+    assert sb(a, b, c, d + 8, e, 4, 8, 0, 0.0, None, None, 0, None, 0) == 2   # grad_x alignment
+    assert sb(a, b, c, d, e + 2, 4, 8, 0, 0.0, None, None, 0, None, 0) == 2   # grad_probs alignment
+    assert sb(a, b, None, d, e, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1    # grad_y required
+    assert sb(a, b, c, None, e, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1    # grad_x required
+    assert sb(a, b, c, c, e, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1       # grad_x over grad_y
+    assert sb(a, b, c, d, b, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1       # grad_probs over probs
+    assert sb(a, b, c, d, d + 16, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1  # outputs overlap
+    assert sb(a, b, c, d, e, 4, 8, 0, 0.0, d, None, 0, None, 0) == 1         # n_used under grad_x
     u = lib.moe_unpermute_expert_order
     assert u(a, 10, b, None, c, 2, 0, 8, 4, None, 0) == 0
     assert u(a, 10, b, None, c, 1, 4, 8, 4, None, 0) == 1                 # fp16 out not supported

@@ -2,9 +2,10 @@
 
 Bars: bitwise where the pages fix the result exactly (residual add = two unfused
 adds; router-weight forward and grad_x = one fp32 product and one rounding;
-squared ReLU without the soft clamp; unpermute = a fixed-order fp32 sum);
-within 1 bf16 ulp for the soft-clamped squared ReLU (tanh is evaluated by
-different fp32 formulas); grad_probs on the row-scale criterion.
+squared ReLU forward and grad_x without the soft clamp; unpermute = a fixed-order
+fp32 sum); within 1 bf16 ulp for the soft-clamped squared ReLU forward and
+backward (tanh and sech^2 are evaluated by different fp32 formulas); grad_probs on
+the row-scale criterion.
 """
 import numpy as np
 import pytest
@@ -12,8 +13,9 @@ import torch
 
 import oracle.moe as moe_oracle
 from bf16cmp import assert_within_ulp, grad_probs_violations
-from memory_bound_elementwise_amd import (FusedMoEResidualAdd, RouterWeightMul, moe_residual_add,
-                                          moe_router_weight_bwd, moe_router_weight_fwd,
+from memory_bound_elementwise_amd import (FusedMoEResidualAdd, RouterWeightMul, SquaredReluProbs,
+                                          moe_residual_add, moe_router_weight_bwd,
+                                          moe_router_weight_fwd, moe_squared_relu_probs_bwd,
                                           moe_squared_relu_probs_fwd, moe_unpermute_expert_order)
 from memory_bound_elementwise_amd.moe_elementwise import load_library
 from parity import say
@@ -208,6 +210,166 @@ def test_squared_relu_rows(zero_padding):
         want = moe_oracle.get().squared_relu_probs(x, p, **kw)
         assert_within_ulp(got, want, 1, f"rows n_used={n_used}")
         assert np.array_equal(got == 0xFFFF, want == 0xFFFF)
+
+
+# ---------------------------------------------------------------------------
+GP_SENTINEL = -12345.5
+
+
+def _sqb_run(x, p, g, with_gp=True, **kw):
+    rows, hidden = x.shape
+    gx = torch.full((rows, hidden), -1, dtype=torch.int16, device=DEV)
+    gp = torch.full((rows,), GP_SENTINEL, dtype=torch.float32, device=DEV) if with_gp else None
+    nu = kw.pop("n_used", None)
+    pm = kw.pop("permutation_map", None)
+    moe_squared_relu_probs_bwd(_dev(x, "bf16").view(torch.int16), torch.from_numpy(p).to(DEV),
+                               _dev(g, "bf16").view(torch.int16), gx, gp,
+                               n_used=None if nu is None else torch.tensor([nu], dtype=torch.int32, device=DEV),
+                               permutation_map=None if pm is None else torch.from_numpy(pm).to(DEV), **kw)
+    torch.cuda.synchronize()
+    return gx.cpu().numpy().view(np.uint16), (None if gp is None else gp.cpu().numpy())
+
+
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def _check_grad_probs(got, want, what):
+    """Rows on the row-scale criterion; rows holding inf / NaN terms must agree in kind
+    (NaN, or the same infinity). Rows whose |terms| add up past the fp32 range are not
+    compared: an fp32 sum may overflow there whatever its order."""
+    scale = want["row_scale"]
+    fin = np.isfinite(want["grad_probs_f64"]) & np.isfinite(scale)
+    ok = fin & (scale < FLT_MAX)
+    bad = grad_probs_violations(got[ok], want["grad_probs_f64"][ok], scale[ok])
+    assert bad.size == 0, f"{what}: grad_probs off on {bad.size} rows"
+    w = want["grad_probs"][~fin]
+    gg = got[~fin]
+    assert np.array_equal(np.isnan(gg), np.isnan(w)) and np.array_equal(gg[np.isinf(w)], w[np.isinf(w)]), \
+        f"{what}: non-finite grad_probs differ"
+
+
+def _check_sqb(gx, gp, want, clamp_scale, what):
+    if clamp_scale is None:
+        assert _same(gx, want["grad_x"], "bf16"), f"{what}: grad_x without clamp must be bit-exact"
+    else:
+        assert_within_ulp(gx, want["grad_x"], 1, what)
+    if gp is not None:
+        _check_grad_probs(gp, want, what)
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 0.5, 4.0, 30.0])
+@pytest.mark.parametrize("rows,hidden", [(7, 8), (513, 1536), (2000, 2048 + 8)])
+def test_squared_relu_bwd(clamp_scale, rows, hidden):
+    rng = np.random.default_rng(rows + 17)
+    x = _rand((rows, hidden), "bf16", rng, 6.0)
+    g = _rand((rows, hidden), "bf16", rng, 1.0, specials=rows != 2000)
+    p = rng.uniform(0, 1, rows).astype(np.float32)
+    gx, gp = _sqb_run(x, p, g, clamp_scale=clamp_scale)
+    want = moe_oracle.get().squared_relu_probs_bwd(x, p, g, clamp_scale=clamp_scale)
+    _check_sqb(gx, gp, want, clamp_scale, f"bwd s={clamp_scale} {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 1.0, 8.0])
+@pytest.mark.parametrize("sweep", ["x", "grad_y"])
+def test_squared_relu_bwd_every_bf16_pattern(clamp_scale, sweep):
+    """All 65,536 bf16 patterns of x (grad_y ~ N(0,1)), or of grad_y (x fixed per row)."""
+    rng = np.random.default_rng(5)
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    other = _rand((256, 256), "bf16", rng, 2.0, specials=False)
+    x, g = (every, other) if sweep == "x" else (other, every)
+    p = np.linspace(0.05, 1.0, 256).astype(np.float32)
+    gx, gp = _sqb_run(x, p, g, clamp_scale=clamp_scale)
+    want = moe_oracle.get().squared_relu_probs_bwd(x, p, g, clamp_scale=clamp_scale)
+    _check_sqb(gx, gp, want, clamp_scale, f"sweep {sweep} s={clamp_scale}")
+
+
+@pytest.mark.parametrize("zero_padding", [False, True])
+def test_squared_relu_bwd_rows(zero_padding):
+    rng = np.random.default_rng(12)
+    rows, hidden = 4096, 1024
+    x = _rand((rows, hidden), "bf16", rng, 3.0, specials=False)
+    g = _rand((rows, hidden), "bf16", rng, 1.0, specials=False)
+    p = rng.uniform(0, 1, rows).astype(np.float32)
+    pm = rng.permutation(rows).astype(np.int32)
+    pm[rng.choice(rows, 40, replace=False)] = -1
+    for clamp_scale in (None, 2.0):
+        for n_used in (0, 1, 3000, rows, rows + 9, -4):
+            kw = dict(clamp_scale=clamp_scale, n_used=n_used, permutation_map=pm, zero_padding=zero_padding)
+            gx, gp = _sqb_run(x, p, g, **kw)
+            want = moe_oracle.get().squared_relu_probs_bwd(x, p, g, **kw)
+            assert np.array_equal(gx == 0xFFFF, want["grad_x"] == 0xFFFF), f"untouched rows n_used={n_used}"
+            assert np.array_equal(gp == GP_SENTINEL, want["grad_probs"] == GP_SENTINEL), \
+                f"untouched grad_probs slots n_used={n_used}"
+            live = want["grad_probs"] != GP_SENTINEL
+            if clamp_scale is None:
+                assert _same(gx, want["grad_x"], "bf16")
+            else:
+                assert_within_ulp(gx, want["grad_x"], 1, f"rows n_used={n_used}")
+            bad = grad_probs_violations(gp[live], want["grad_probs_f64"][live], want["row_scale"][live])
+            assert bad.size == 0
+    # without grad_probs only grad_x is written
+    gx, _ = _sqb_run(x, p, g, with_gp=False, clamp_scale=2.0)
+    assert_within_ulp(gx, moe_oracle.get().squared_relu_probs_bwd(x, p, g, clamp_scale=2.0)["grad_x"], 1, "no gp")
+
+
+def test_squared_relu_bwd_grid_invariant():
+    """grad_x and grad_probs bits do not depend on the workgroup count, run to run."""
+    rng = np.random.default_rng(13)
+    rows, hidden = 3001, 2048
+    x = _rand((rows, hidden), "bf16", rng, 3.0, specials=False)
+    g = _rand((rows, hidden), "bf16", rng, 1.0, specials=False)
+    p = rng.uniform(0, 1, rows).astype(np.float32)
+    for s in (None, 4.0):
+        ref = None
+        for nwg in (0, 1, 37, 256, 1024, 0):
+            gx, gp = _sqb_run(x, p, g, clamp_scale=s, num_workgroups=nwg)
+            if ref is None:
+                ref = (gx, gp)
+                _check_sqb(gx, gp, moe_oracle.get().squared_relu_probs_bwd(x, p, g, clamp_scale=s), s, "grid")
+            else:
+                assert np.array_equal(gx, ref[0]) and np.array_equal(gp.view(np.uint32), ref[1].view(np.uint32)), \
+                    f"grid {nwg} changed bits (s={s})"
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 4.0])
+def test_squared_relu_autograd(clamp_scale):
+    rng = np.random.default_rng(14)
+    rows, hidden = 300, 512
+    x = _rand((rows, hidden), "bf16", rng, 3.0, specials=False)
+    g = _rand((rows, hidden), "bf16", rng, 1.0, specials=False)
+    p = rng.uniform(0, 1, (rows, 1)).astype(np.float32)
+    tx = _dev(x, "bf16").requires_grad_(True)
+    tp = torch.from_numpy(p).to(DEV).requires_grad_(True)
+    y = SquaredReluProbs.apply(tx, tp, clamp_scale)
+    y.backward(_dev(g, "bf16"))
+    orc = moe_oracle.get()
+    assert_within_ulp(_host(y.detach(), "bf16"), orc.squared_relu_probs(x, p, clamp_scale=clamp_scale), 1, "fwd")
+    want = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=clamp_scale)
+    _check_sqb(_host(tx.grad, "bf16"), tp.grad.reshape(-1).cpu().numpy(), want, clamp_scale, "autograd")
+    assert tp.grad.shape == tp.shape
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 4.0])
+def test_squared_relu_bwd_full_size_sampled(clamp_scale):
+    """53,760 x 2,048 (the MoE workload), default launch; sampled rows against the oracle."""
+    from memory_bound_elementwise_amd.workloads import make_moe_inputs
+    inp = make_moe_inputs("squared_relu", seed=0)
+    x, p = inp["x"], inp["probs"]
+    rows, hidden = x.shape
+    g = torch.Generator(device=DEV).manual_seed(9)
+    gy = torch.randn(rows, hidden, device=DEV, generator=g).to(torch.bfloat16)
+    xd = _dev(x, "bf16")
+    gx = torch.empty_like(xd)
+    gp = torch.full((rows,), GP_SENTINEL, device=DEV)
+    say(f"[sqrelu bwd full] s={clamp_scale} {rows}x{hidden}")
+    moe_squared_relu_probs_bwd(xd, torch.from_numpy(p).to(DEV), gy, gx, gp, clamp_scale=clamp_scale)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(3), np.arange(rows - 200, rows),
+                                    np.random.default_rng(1).integers(0, rows, 300)]))
+    ti = torch.from_numpy(idx).to(DEV)
+    gys = _host(gy[ti], "bf16")
+    want = moe_oracle.get().squared_relu_probs_bwd(x[idx], p[idx], gys, clamp_scale=clamp_scale)
+    _check_sqb(_host(gx[ti], "bf16"), gp[ti].cpu().numpy(), want, clamp_scale, "full size")
 
 
 # ---------------------------------------------------------------------------

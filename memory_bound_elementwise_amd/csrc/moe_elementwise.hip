@@ -470,16 +470,16 @@ struct SquaredReluBwdOp {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const float z = __builtin_elementwise_maximum(v[i] * inv_s, 0.0f);
-                // v_exp_f32 flushes subnormal results: e^(-2z) * 2^64 is formed instead
-                // and scaled back by a multiply, which keeps e (and so sech^2) down to
-                // the smallest subnormal, as the fp32 chain has it
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z, kNeg2Log2e, 64.0f)) * 0x1p-64f;
-                const float r = __builtin_amdgcn_rcpf(1.0f + e);
+                // v_exp_f32 flushes subnormal results, so E * 2^64 is formed instead and
+                // the 2^-64 goes into the fmas and the multiply that use it: sech^2
+                // keeps its value down to the smallest subnormal, as the fp32 chain has it
+                const float e64 = __builtin_amdgcn_exp2f(__builtin_fmaf(z, kNeg2Log2e, 64.0f));
+                const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(e64, 0x1p-64f, 1.0f));
                 const float u = z * z;
                 const float small = z * __builtin_fmaf(u, __builtin_fmaf(u, kTwoFifteenths, kThird), 1.0f);
-                const float t = z < 0.125f ? small : (1.0f - e) * r;
+                const float t = z < 0.125f ? small : __builtin_fmaf(-e64, 0x1p-64f, 1.0f) * r;
                 const float a = s * t;
-                const float sech2 = ((4.0f * e) * r) * r;
+                const float sech2 = ((e64 * 0x1p-62f) * r) * r;  // 4 E r^2
                 ypre[i] = a * a;
                 grad[i] = ((gv[i] * p) * (2.0f * a)) * sech2;
             }
@@ -769,16 +769,20 @@ void launch_sqrelu_bwd(int U, int blocks, hipStream_t st, const uint16_t *x, con
 #ifndef MOE_UNPERMUTE_BPC
 #define MOE_UNPERMUTE_BPC 2
 #endif
-#ifndef MOE_SQRELU_BPC
-#define MOE_SQRELU_BPC 2
+#ifndef MOE_SQRELU_CLAMP_BPC
+#define MOE_SQRELU_CLAMP_BPC 8
 #endif
 constexpr int kUnpermuteU = MOE_UNPERMUTE_U;
 constexpr int kUnpermuteG = MOE_UNPERMUTE_G;
 // The unpermute waits on each group of gathers before adding it, so it keeps more
 // waves resident than the pure streams do.
 constexpr int kUnpermuteBlocksPerCU = MOE_UNPERMUTE_BPC;
-// The soft-clamped squared ReLU is vector-ALU bound (about 17 operations per element).
-constexpr int kSquaredReluBlocksPerCU = MOE_SQRELU_BPC;
+// The soft-clamped squared ReLU (forward ~17, backward ~30 vector operations per
+// element) is ALU bound: it launches more workgroups than stay resident (3 per CU at
+// the backward's register use), so those that finish early take the remaining rows.
+// Without the clamp it is a plain stream and keeps one workgroup per CU.
+constexpr int kSquaredReluClampBlocksPerCU = MOE_SQRELU_CLAMP_BPC;
+constexpr int kSquaredReluPlainBlocksPerCU = 1;
 
 }  // namespace
 
@@ -929,7 +933,8 @@ moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, u
         return fail_hip(he);
     const int U = pick_u(hidden / 8);
     const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : balanced_workgroups(rows, cus * kSquaredReluBlocksPerCU, 1);
+                                          : balanced_workgroups(rows, cus * (clamp ? kSquaredReluClampBlocksPerCU
+                                                                                   : kSquaredReluPlainBlocksPerCU), 1);
     const float s = clamp ? clamp_scale : 1.0f;
     if (clamp)
         launch_sqrelu<true>(U, blocks, stream, x, probs, y, (int)rows, (int)hidden, s, 1.0f / s, n_used,
@@ -975,7 +980,8 @@ moe_status_t moe_squared_relu_probs_bwd(const uint16_t *x, const float *probs, c
         return fail_hip(he);
     const int U = pick_u(hidden / 8);
     const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : balanced_workgroups(rows, cus * kSquaredReluBlocksPerCU, 1);
+                                          : balanced_workgroups(rows, cus * (clamp ? kSquaredReluClampBlocksPerCU
+                                                                                   : kSquaredReluPlainBlocksPerCU), 1);
     const float s = clamp ? clamp_scale : 1.0f;
     if (clamp)
         launch_sqrelu_bwd<true>(U, blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows,

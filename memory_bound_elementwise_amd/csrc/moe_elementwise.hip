@@ -600,6 +600,146 @@ __global__ __launch_bounds__(kBlock) void unpermute_kernel(const uint16_t *eo, i
     }
 }
 
+// The same reduction for up to G local experts, pipelined. A wave walks its units
+// (token, chunk) in order. All G gathers of the next unit are issued before the
+// current unit is added and stored, so one memory latency is exposed per wave, not
+// one per chunk, also across token boundaries. One load fetches the map rows of the
+// wave's next 64 / G tokens (lane l holds entry l % G of token l / G), so the
+// pipeline waits on the map once per 64 / G tokens.
+//
+// With fp32 output, a lane's eight elements are two groups of four, elements
+// 4l .. 4l+3 of two adjacent 256-element blocks (two 8-byte loads), so each of the
+// two 16-byte fp32 stores writes 1 KiB contiguous across the wave. The plain layout
+// (eight consecutive elements, one 16-byte load) would give each store instruction
+// every other 16 bytes of a 2 KiB span: half-written lines, which measured about
+// twice the write cost. The adds run in the same order either way.
+template <int U, int G>
+struct UnpermuteBuf {
+    u32x4 v[G][U];
+};
+
+template <int ODT, int U, int G>
+__global__ __launch_bounds__(kBlock) void unpermute_pipelined_kernel(const uint16_t *eo, int64_t erows,
+                                                                     const int *map, const int *valid_tokens,
+                                                                     char *out, int tokens, int hidden, int E)
+{
+    constexpr int kTokensPerMap = kWave / G;
+    constexpr bool kSplit = ODT == DT_F32;
+    const int lane = lane_id();
+    const int64_t W = (int64_t)gridDim.x * kWavesPerBlock;
+    int bound = tokens;
+    if (valid_tokens) {
+        const int v = *valid_tokens;
+        bound = v < 0 ? 0 : (v > tokens ? tokens : v);
+    }
+    const uint32_t row = (uint32_t)hidden * 2u;
+    const uint32_t orow = (uint32_t)hidden * kElemBytes<ODT>;
+    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
+    const uint32_t chunk = (uint32_t)U * kWave * kVecBytes;
+    const int erows32 = (int)erows;  // below 2^31 (checked on the host): a scalar compare
+
+    // map entries of tokens t0 + j W, j < kTokensPerMap; -1 past E or past the bound
+    auto load_maps = [&](int64_t t0) -> int {
+        const int64_t tok = t0 + (int64_t)(lane / G) * W;
+        const int e = lane % G;
+        const bool ok = e < E && tok < bound;
+        const int v = map[ok ? tok * E + e : 0];
+        return ok ? v : -1;
+    };
+    auto issue = [&](UnpermuteBuf<U, G> &b, int c, int mvs, int j) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int m = __builtin_amdgcn_readlane(mvs, j * G + g);
+            const bool ok = m >= 0 && m < erows32;
+            const rsrc_t rs = chunk_rsrc(eo + (int64_t)(ok ? m : 0) * hidden, ok ? row : 0u, (uint32_t)c * chunk);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if constexpr (kSplit) {
+                    const uint32_t o = (uint32_t)u * kWave * kVecBytes + (uint32_t)lane * 8u;
+                    const auto lo = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, CDNA4_LOAD_AUX);
+                    const auto hi = __builtin_amdgcn_raw_buffer_load_b64(rs, o + kWave * 8u, 0, CDNA4_LOAD_AUX);
+                    b.v[g][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    b.v[g][u] = load_vec(rs, (uint32_t)(lane + u * kWave) * kVecBytes);
+                }
+            }
+        }
+    };
+    auto finish = [&](const UnpermuteBuf<U, G> &b, int64_t tok, int c) {
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[u][i] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[u][2 * q] = acc[u][2 * q] + bf16_lo(b.v[g][u][q]);
+                    acc[u][2 * q + 1] = acc[u][2 * q + 1] + bf16_hi(b.v[g][u][q]);
+                }
+        const rsrc_t ro = chunk_rsrc(out + tok * orow, orow, (uint32_t)c * U * kWave * kOctBytes<ODT>);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (kSplit) {
+                const uint32_t o = (uint32_t)u * kWave * 32u + (uint32_t)lane * 16u;
+                store_vec(ro, u32x4{__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]),
+                                    __float_as_uint(acc[u][2]), __float_as_uint(acc[u][3])}, o);
+                store_vec(ro, u32x4{__float_as_uint(acc[u][4]), __float_as_uint(acc[u][5]),
+                                    __float_as_uint(acc[u][6]), __float_as_uint(acc[u][7])}, o + kWave * 16u);
+            } else {
+                store_oct<ODT>(ro, narrow<ODT>(acc[u]), (lane + u * kWave) * kOctBytes<ODT>);
+            }
+        }
+    };
+
+    // current unit (t, c), token t being entry j of the map group held in mvs
+    int64_t t = wave_id();
+    if (t >= bound)
+        return;
+    int mvs = load_maps(t);
+    int j = 0, c = 0;
+    // the next unit's chunk and map slot; a new map group is loaded when the next
+    // token starts one (its gathers need it at once)
+    int c1, j1, mvs1;
+    auto step = [&]() {
+        if (c + 1 < nch) {
+            c1 = c + 1, j1 = j, mvs1 = mvs;
+        } else if (j + 1 < kTokensPerMap) {
+            c1 = 0, j1 = j + 1, mvs1 = mvs;
+        } else {
+            c1 = 0, j1 = 0, mvs1 = load_maps(t + W);
+        }
+    };
+    auto advance = [&]() {
+        t = c1 == 0 ? t + W : t;
+        c = c1, j = j1, mvs = mvs1;
+    };
+    // The scheduling barriers keep each unit's gathers ahead of the previous unit's
+    // adds: the two are independent, and the scheduler would otherwise sink the loads.
+    UnpermuteBuf<U, G> A, B;
+    issue(A, 0, mvs, 0);
+    for (;;) {
+        step();
+        issue(B, c1, mvs1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(A, t, c);
+        advance();
+        if (t >= bound)
+            break;
+        step();
+        issue(A, c1, mvs1, j1);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(B, t, c);
+        advance();
+        if (t >= bound)
+            break;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -772,11 +912,25 @@ void launch_sqrelu_bwd(int U, int blocks, hipStream_t st, const uint16_t *x, con
 #ifndef MOE_SQRELU_CLAMP_BPC
 #define MOE_SQRELU_CLAMP_BPC 8
 #endif
+#ifndef MOE_UNPERMUTE_PIPE_U
+#define MOE_UNPERMUTE_PIPE_U 2
+#endif
+#ifndef MOE_UNPERMUTE_PIPE_BPC
+#define MOE_UNPERMUTE_PIPE_BPC 1
+#endif
+#ifndef MOE_UNPERMUTE_PIPELINED
+#define MOE_UNPERMUTE_PIPELINED 1
+#endif
 constexpr int kUnpermuteU = MOE_UNPERMUTE_U;
 constexpr int kUnpermuteG = MOE_UNPERMUTE_G;
 // The unpermute waits on each group of gathers before adding it, so it keeps more
 // waves resident than the pure streams do.
 constexpr int kUnpermuteBlocksPerCU = MOE_UNPERMUTE_BPC;
+// Up to this many local experts take the pipelined unpermute, one workgroup per CU
+// (measured best: 110 us against 113 us at two, for 6720 tokens x 8 experts).
+constexpr int kUnpermutePipelinedMaxExperts = MOE_UNPERMUTE_PIPELINED ? 8 : 0;
+constexpr int kUnpermutePipeU = MOE_UNPERMUTE_PIPE_U;
+constexpr int kUnpermutePipeBlocksPerCU = MOE_UNPERMUTE_PIPE_BPC;
 // The soft-clamped squared ReLU (forward ~17, backward ~30 vector operations per
 // element) is ALU bound: it launches more workgroups than stay resident (3 per CU at
 // the backward's register use), so those that finish early take the remaining rows.
@@ -1022,9 +1176,27 @@ moe_status_t moe_unpermute_expert_order(const uint16_t *expert_output, int64_t e
     hipError_t he = device_cus(&cus);
     if (he != hipSuccess)
         return fail_hip(he);
-    int resident = kUnpermuteBlocksPerCU;
+    const bool pipelined = num_local_experts <= kUnpermutePipelinedMaxExperts;
+    const int resident = pipelined ? kUnpermutePipeBlocksPerCU : kUnpermuteBlocksPerCU;
     const int blocks = num_workgroups > 0 ? num_workgroups
                                           : balanced_workgroups(tokens, cus * resident, 1);
+    if (pipelined) {
+        char *o = static_cast<char *>(out);
+        const int T32 = (int)tokens, H32 = (int)hidden, E = num_local_experts;
+        if (out_dtype == MOE_FP32 && E <= 4)
+            hipLaunchKernelGGL((unpermute_pipelined_kernel<DT_F32, kUnpermutePipeU, 4>), dim3(blocks), dim3(kBlock),
+                               0, stream, expert_output, expert_rows, inverse_map, valid_tokens, o, T32, H32, E);
+        else if (out_dtype == MOE_FP32)
+            hipLaunchKernelGGL((unpermute_pipelined_kernel<DT_F32, kUnpermutePipeU, 8>), dim3(blocks), dim3(kBlock),
+                               0, stream, expert_output, expert_rows, inverse_map, valid_tokens, o, T32, H32, E);
+        else if (E <= 4)
+            hipLaunchKernelGGL((unpermute_pipelined_kernel<DT_BF16, kUnpermutePipeU, 4>), dim3(blocks), dim3(kBlock),
+                               0, stream, expert_output, expert_rows, inverse_map, valid_tokens, o, T32, H32, E);
+        else
+            hipLaunchKernelGGL((unpermute_pipelined_kernel<DT_BF16, kUnpermutePipeU, 8>), dim3(blocks), dim3(kBlock),
+                               0, stream, expert_output, expert_rows, inverse_map, valid_tokens, o, T32, H32, E);
+        return launched();
+    }
     if (out_dtype == MOE_FP32)
         hipLaunchKernelGGL((unpermute_kernel<DT_F32, kUnpermuteU, kUnpermuteG>), dim3(blocks), dim3(kBlock), 0,
                            stream, expert_output, expert_rows, inverse_map, valid_tokens,

@@ -400,6 +400,57 @@ def test_unpermute(out_dt, tokens, E, hidden):
     assert _same(_host(out, out_dt), want, out_dt), "unpermute must be bit-exact (fixed order)"
 
 
+@pytest.mark.parametrize("E", [2, 3, 5, 6, 7])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_unpermute_experts_below_group(E, out_dt):
+    """Expert counts that leave part of the 4- or 8-wide gather group empty."""
+    rng = np.random.default_rng(100 + E)
+    tokens, hidden = 777, 1032
+    eo, im = _unpermute_inputs(rng, tokens, E, hidden, 0.6)
+    want = moe_oracle.get().unpermute(eo, im, out_dt)
+    out = torch.empty((tokens, hidden), dtype=TD[out_dt], device=DEV)
+    moe_unpermute_expert_order(_dev(eo, "bf16"), torch.from_numpy(im).to(DEV), out)
+    torch.cuda.synchronize()
+    assert _same(_host(out, out_dt), want, out_dt)
+
+
+@pytest.mark.parametrize("E", [4, 8, 12])
+def test_unpermute_grid_invariant(E):
+    """Same bits for any workgroup count, including one workgroup (every wave walks
+    hundreds of tokens and reloads its map rows many times)."""
+    rng = np.random.default_rng(200 + E)
+    tokens, hidden = 2048, 520
+    eo, im = _unpermute_inputs(rng, tokens, E, hidden, 0.5)
+    want = moe_oracle.get().unpermute(eo, im, "f32")
+    eod, imd = _dev(eo, "bf16"), torch.from_numpy(im).to(DEV)
+    vt = torch.tensor([tokens - 5], dtype=torch.int32, device=DEV)
+    for nwg in (1, 3, 240, 256, 1024, 0):
+        out = torch.full((tokens, hidden), float("nan"), device=DEV)
+        moe_unpermute_expert_order(eod, imd, out, valid_tokens=vt, num_workgroups=nwg)
+        torch.cuda.synchronize()
+        o = _host(out, "f32")
+        assert _same(o[:tokens - 5], want[:tokens - 5], "f32"), f"grid {nwg}"
+        assert np.all(np.isnan(o[tokens - 5:])), f"grid {nwg}: tokens past the bound written"
+
+
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_unpermute_full_size_sampled(out_dt):
+    """6720 tokens x 8 local experts x 7168 (the MoE workload), default launch; sampled
+    tokens against the oracle on the rows they gather."""
+    from memory_bound_elementwise_amd.workloads import make_moe_inputs
+    inp = make_moe_inputs("unpermute", seed=0)
+    eo, im = inp["expert_output"], inp["inverse_map"]
+    tokens, hidden = im.shape[0], eo.shape[1]
+    say(f"[unpermute full] {tokens}x{im.shape[1]}x{hidden} {out_dt}")
+    out = torch.empty((tokens, hidden), dtype=TD[out_dt], device=DEV)
+    moe_unpermute_expert_order(_dev(eo, "bf16"), torch.from_numpy(im).to(DEV), out)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(3), np.arange(tokens - 100, tokens),
+                                    np.random.default_rng(2).integers(0, tokens, 300)]))
+    want = moe_oracle.get().unpermute(eo, im[idx], out_dt)
+    assert _same(_host(out, out_dt)[idx], want, out_dt)
+
+
 def test_unpermute_order_and_bound():
     hidden = 64
     big = np.zeros((3, hidden), np.uint16)

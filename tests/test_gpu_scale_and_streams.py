@@ -11,9 +11,9 @@ import torch
 import oracle
 import oracle.moe as moe_oracle
 from bf16cmp import grad_probs_violations, ulp_distance
-from memory_bound_elementwise_amd import (moe_residual_add, moe_squared_relu_probs_fwd,
-                                          moe_unpermute_expert_order, swiglu_probs_bwd,
-                                          swiglu_probs_fwd)
+from memory_bound_elementwise_amd import (moe_residual_add, moe_squared_relu_probs_bwd,
+                                          moe_squared_relu_probs_fwd, moe_unpermute_expert_order,
+                                          swiglu_probs_bwd, swiglu_probs_fwd)
 from parity import say
 
 pytestmark = pytest.mark.gpu
@@ -55,13 +55,17 @@ def test_activation_past_4gib():
 
 
 def test_moe_ops_graph_replay():
-    """One graph holding the squared ReLU (device n_used) and the unpermute (device
-    valid_tokens); both counts change between replays, with eager work in between."""
+    """One graph holding the squared ReLU forward and backward (device n_used) and the
+    unpermute (device valid_tokens); both counts change between replays, with eager work
+    in between."""
     rng = np.random.default_rng(3)
     rows, hidden, E = 4096, 1024, 8
     x = torch.from_numpy(rng.standard_normal((rows, hidden)).astype(np.float32) * 3).to(torch.bfloat16).to(DEV)
     p = torch.from_numpy(rng.uniform(0, 1, rows).astype(np.float32)).to(DEV)
+    gy = torch.from_numpy(rng.standard_normal((rows, hidden)).astype(np.float32)).to(torch.bfloat16).to(DEV)
     y = torch.empty_like(x)
+    gx = torch.empty_like(x)
+    gp = torch.empty_like(p)
     n_used = torch.tensor([rows], dtype=torch.int32, device=DEV)
     tokens = 512
     valid = rng.random((tokens, E)) < 0.5
@@ -78,6 +82,7 @@ def test_moe_ops_graph_replay():
 
     def run():
         moe_squared_relu_probs_fwd(x, p, y, clamp_scale=3.0, n_used=n_used, zero_padding=True)
+        moe_squared_relu_probs_bwd(x, p, gy, gx, gp, clamp_scale=3.0, n_used=n_used, zero_padding=True)
         moe_unpermute_expert_order(eo, imd, out, valid_tokens=vt)
 
     s = torch.cuda.Stream()
@@ -91,17 +96,27 @@ def test_moe_ops_graph_replay():
         run()
     orc = moe_oracle.get()
     xb = _bits(x)
+    gyb = _bits(gy)
     eob = _bits(eo)
     for nu, v in ((rows, tokens), (1000, 17), (0, 0), (rows - 1, tokens - 1)):
         n_used.fill_(nu)
         vt.fill_(v)
         y.fill_(float("nan"))
+        gx.fill_(float("nan"))
+        gp.fill_(-12345.5)
         out.fill_(-1.0)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         want_y = orc.squared_relu_probs(xb, p.cpu().numpy(), clamp_scale=3.0, n_used=nu, zero_padding=True)
         assert ulp_distance(_bits(y), want_y).max() <= 1, f"replay n_used={nu}"
+        want_b = orc.squared_relu_probs_bwd(xb, p.cpu().numpy(), gyb, clamp_scale=3.0, n_used=nu,
+                                            zero_padding=True)
+        assert ulp_distance(_bits(gx), want_b["grad_x"]).max() <= 1, f"replay bwd n_used={nu}"
+        g = gp.cpu().numpy()
+        assert np.all(g[nu:] == -12345.5), f"replay bwd n_used={nu}: slots past n_used written"
+        bad = grad_probs_violations(g[:nu], want_b["grad_probs_f64"][:nu], want_b["row_scale"][:nu])
+        assert bad.size == 0, f"replay bwd n_used={nu}: grad_probs"
         want_o = orc.unpermute(eob, im, "f32", valid_tokens=v,
                                out=np.full((tokens, hidden), -1.0, np.float32))
         assert np.array_equal(out.cpu().numpy().view(np.uint32), want_o.view(np.uint32)), f"replay valid={v}"

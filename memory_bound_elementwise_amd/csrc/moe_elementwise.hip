@@ -794,10 +794,21 @@ bool dtype_ok(moe_dtype_t d) { return d == MOE_BF16 || d == MOE_FP16 || d == MOE
 constexpr int64_t kMaxRows = 0x7fffffffLL - 64LL * 65536LL;
 constexpr int64_t kMaxHidden = 1LL << 26;  // a row stays under 2^32 bytes in fp32
 
+// Octs per lane per chunk: the U in 1..4 that leaves the fewest idle lane slots in a
+// row's last chunk, ties to the larger U (7168 columns: U = 2, seven full chunks, not
+// four chunks of which the last is half empty). A lane's octs are lane + 64 k in
+// increasing k for every U, so row sums do not depend on the choice.
 int pick_u(int64_t octs)
 {
     const int64_t u = (octs + kWave - 1) / kWave;
-    return u >= 4 ? 4 : (u < 1 ? 1 : (int)u);
+    int best = 1;
+    int64_t best_waste = INT64_MAX;
+    for (int c = 4; c >= 1; --c) {
+        const int64_t waste = (u + c - 1) / c * c - u;
+        if (waste < best_waste)
+            best = c, best_waste = waste;
+    }
+    return best;
 }
 
 moe_status_t launched()

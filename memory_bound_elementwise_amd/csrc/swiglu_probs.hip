@@ -302,10 +302,20 @@ hipError_t device_info(DeviceLaunchInfo **out)
     return info.err;
 }
 
+// Vectors per lane per chunk: the U in 1..kMaxU that leaves the fewest idle lane slots
+// in a row's last chunk, ties to the larger U. A lane's vectors are lane + 64 k in
+// increasing k for every U, so the probability gradient does not depend on the choice.
 int pick_u(int64_t vpr)
 {
-    int64_t u = (vpr + kWave - 1) / kWave;
-    return u >= kMaxU ? kMaxU : (u < 1 ? 1 : (int)u);
+    const int64_t u = (vpr + kWave - 1) / kWave;
+    int best = 1;
+    int64_t best_waste = INT64_MAX;
+    for (int c = kMaxU; c >= 1; --c) {
+        const int64_t waste = (u + c - 1) / c * c - u;
+        if (waste < best_waste)
+            best = c, best_waste = waste;
+    }
+    return best;
 }
 
 // Workgroups so that the resident waves divide the rows evenly: with R rows and at

@@ -52,8 +52,8 @@ def soft_clamp_relu_fp32(x, s, p, q, umax):
     x = np.asarray(x, f32)
     s = f32(s)
     inv_s = f32(1.0) / s
-    z = (x * inv_s).astype(f32)
-    with np.errstate(over="ignore", invalid="ignore"):
+    with np.errstate(over="ignore", invalid="ignore"):   # +-inf inputs and overflow are part of the check
+        z = (x * inv_s).astype(f32)
         u = np.fmin((z * z).astype(f32), f32(umax))
         pn = _fma(_fma(_fma(np.full_like(u, p[3]), u, p[2]), u, p[1]), u, p[0])
         qd = _fma(_fma(_fma(np.full_like(u, q[3]), u, q[2]), u, q[1]), u, f32(1.0))

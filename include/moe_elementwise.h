@@ -21,7 +21,8 @@
  *     allocation, no host read of device data: calls are hipGraph-capturable.
  *   - Arguments are checked on the host before anything is launched; on error nothing
  *     is written.
- *   - num_workgroups: 0 = the library's choice (one workgroup per CU, rows balanced
+ *   - num_workgroups: 0 = the library's choice (one wave per row or block when a row
+ *     is at most two column chunks, else one workgroup per CU with the rows balanced
  *     over the waves); any positive count gives the same result bits.
  *   - The library keeps no pointer after a call returns; calls are thread-safe.
  */

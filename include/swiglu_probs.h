@@ -123,7 +123,9 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
                                     int zero_padding, hipStream_t stream, int num_workgroups);
 
 /* Workgroup count the library would launch for this call shape on the current
- * device (direction 0 = forward, 1 = backward), or -1 on error. Host only. */
+ * device (direction 0 = forward, 1 = backward), or -1 on error. Host only.
+ * Rows of at most two column chunks (inter <= 4096 for bf16) get one wave per row,
+ * ceil(rows / 4) workgroups; longer rows one workgroup per CU, balanced. */
 int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter);
 
 /* Static text for a status code. Never NULL. */

@@ -278,6 +278,29 @@ inline int balanced_workgroups(int64_t units, int cus, int resident_blocks_per_c
     return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
+// Default grid of a walk over `units` rows (or blocks) of `chunks` chunks each.
+//   * Units of one or two chunks: one wave per unit, ceil(units / 4) workgroups, which
+//     the dispatcher starts as slots free up. The rows in flight then stay one
+//     contiguous window of the arrays. Measured on MI355X at 53760 x 2048: activation
+//     forward 6.38 and backward 6.28 TB/s, against 6.10 / 5.76 TB/s with one persistent
+//     workgroup per CU; the plain streaming probe gains alike (2:1 6.26 -> 6.50, 3:2
+//     6.15 -> 6.31 TB/s). Grids of 4 to 16 persistent workgroups per CU were slower
+//     than either.
+//   * Longer units: one persistent workgroup per CU (at most `resident_blocks_per_cu`),
+//     balanced over the units, so each wave's two-buffer pipeline overlaps its own
+//     chunks. For 7168-column rows (7 chunks) this was 2-4% faster than one wave per row.
+// The grid depends only on host sizes, never on device data.
+constexpr int64_t kPerWaveMaxChunks = 2;
+
+inline int walk_workgroups(int64_t units, int64_t chunks, int cus, int resident_blocks_per_cu)
+{
+    if (units <= 0)
+        return 1;
+    if (chunks <= kPerWaveMaxChunks)
+        return (int)((units + kWavesPerBlock - 1) / kWavesPerBlock);
+    return balanced_workgroups(units, cus, resident_blocks_per_cu);
+}
+
 }  // namespace cdna4
 
 #endif  // MBE_CDNA4_STREAM_H

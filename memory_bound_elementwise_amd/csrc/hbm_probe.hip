@@ -5,7 +5,7 @@
 // wave streams 4 KiB blocks of every source (64 lanes x 4 x 16-byte buffer loads
 // with the nontemporal hint), blocks interleaved across waves, through the same
 // two-buffer pipeline (the next block's loads issued before the current block's
-// stores), with one workgroup per CU. Destination vector i is the XOR of the source
+// stores), with the kernels' default grid (one wave per block). Destination vector i is the XOR of the source
 // vectors i.
 #include <hip/hip_runtime.h>
 
@@ -88,8 +88,8 @@ int launch(const Ptrs &p, int64_t n_vec, int blocks, hipStream_t stream)
         hipDeviceProp_t prop;
         if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return 3;
-        blocks = balanced_workgroups((n_vec * kVecBytes + kBlockBytes - 1) / kBlockBytes,
-                                     prop.multiProcessorCount, 1);
+        blocks = walk_workgroups((n_vec * kVecBytes + kBlockBytes - 1) / kBlockBytes, 1,
+                                 prop.multiProcessorCount, 1);
     }
     hipLaunchKernelGGL((stream_kernel<NS, ND>), dim3(blocks), dim3(kBlock), 0, stream, p, n_vec);
     return hipGetLastError() == hipSuccess ? 0 : 3;

@@ -318,8 +318,10 @@ int pick_u(int64_t vpr)
     return best;
 }
 
-// Workgroups so that the resident waves divide the rows evenly: with R rows and at
-// most M resident waves, rounds = ceil(R / M) and W = ceil(R / rounds) waves.
+// Column chunks of a row: U vectors per lane, 64 lanes.
+int64_t chunks_per_row(int64_t vpr, int U) { return (vpr + (int64_t)U * kWave - 1) / ((int64_t)U * kWave); }
+
+// Address ranges, for the check that no output overlaps an input.
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
 };
@@ -417,7 +419,8 @@ swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint1
     const int vpr = (int)(inter / 8);
     const int U = pick_u(vpr);
     const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : balanced_workgroups(rows, info->cus, info->fwd_blocks_per_cu[U]);
+                                          : walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
+                                                            info->fwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
     switch (U) {
     case 1: launch_fwd<1>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
@@ -465,7 +468,8 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
     const int vpr = (int)(inter / 8);
     const int U = pick_u(vpr);
     const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : balanced_workgroups(rows, info->cus, info->bwd_blocks_per_cu[U]);
+                                          : walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
+                                                            info->bwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
     switch (U) {
     case 1: launch_bwd<1>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
@@ -507,7 +511,7 @@ int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter)
         return -1;
     const int U = pick_u(inter / 8);
     const int bpc = direction == 0 ? info->fwd_blocks_per_cu[U] : info->bwd_blocks_per_cu[U];
-    return balanced_workgroups(rows, info->cus, bpc);
+    return walk_workgroups(rows, chunks_per_row(inter / 8, U), info->cus, bpc);
 }
 
 const char *swiglu_probs_status_string(swiglu_status_t status)

@@ -89,12 +89,17 @@ def test_dummy_map_entries(zero_padding):
     check_parity(inp, label=f"dummy entries zero_padding={zero_padding}")
 
 
-def test_default_workgroups_balanced():
+def test_default_workgroups():
+    """Rows of at most two column chunks: one wave per row. Longer rows: at most one
+    workgroup per CU, with no round of rows left mostly idle."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = WORKLOADS["headline"].rows
     for d in ("fwd", "bwd"):
-        wg = swiglu_probs_default_workgroups(d, WORKLOADS["headline"].rows, WORKLOADS["headline"].inter)
+        wg = swiglu_probs_default_workgroups(d, rows, WORKLOADS["headline"].inter)
+        say(f"[launch] {d} inter {WORKLOADS['headline'].inter}: {wg} workgroups")
+        assert wg == -(-rows // 4)
+        wg = swiglu_probs_default_workgroups(d, rows, 8192)      # 16 vectors per lane: 4 chunks
         waves = wg * 4
-        rounds = -(-WORKLOADS["headline"].rows // waves)
-        say(f"[launch] {d}: {wg} workgroups on {cus} CUs, {rounds} row rounds")
-        # at most one workgroup per CU, and no round of rows left mostly idle
-        assert cus // 2 <= wg <= cus and rounds * waves - WORKLOADS["headline"].rows < waves
+        rounds = -(-rows // waves)
+        say(f"[launch] {d} inter 8192: {wg} workgroups on {cus} CUs, {rounds} row rounds")
+        assert cus // 2 <= wg <= cus and rounds * waves - rows < waves

@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import platform
@@ -49,10 +50,15 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash(paths=None) -> str:
+    """sha256[:16] of the kernel sources' code: comments and whitespace are left out, so
+    a counter summary stays valid across edits that change no instruction."""
     h = hashlib.sha256()
     for p in (paths or KERNEL_SRC):
-        with open(p, "rb") as fh:
-            h.update(fh.read())
+        with open(p) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -945,14 +945,13 @@ constexpr int kUnpermuteBlocksPerCU = MOE_UNPERMUTE_BPC;
 constexpr int kUnpermutePipelinedMaxExperts = MOE_UNPERMUTE_PIPELINED ? 8 : 0;
 constexpr int kUnpermutePipeU = MOE_UNPERMUTE_PIPE_U;
 constexpr int kUnpermutePipeBlocksPerCU = MOE_UNPERMUTE_PIPE_BPC;
-// The soft-clamped squared ReLU (forward ~18, backward ~29 vector instructions per
-// element) keeps the VALU 60-70% busy. With one workgroup per CU its waves cannot hide
-// that behind the loads. It runs instead with 2 octs per lane per chunk (83 registers,
-// up to 6 waves per SIMD) and one wave per row, ceil(rows / 4) workgroups dispatched as
-// slots free up. Measured at 53760 x 2048: forward 72.6 us and backward 103.8 us,
-// level with the unclamped kernels, against 81.9 / 118.9 us with a balanced grid of
-// 1920 resident-sized workgroups, whose last dispatch round ran half empty. Without
-// the clamp the kernel is a plain stream and keeps one workgroup per CU.
+// The soft-clamped squared ReLU (forward ~19, backward ~30 vector instructions per
+// element) keeps the VALU 74% / 86% busy. It runs with 2 octs per lane per chunk
+// (83 registers, up to 6 waves per SIMD) and one wave per row whatever the row length.
+// Measured at 53760 x 2048: forward 72.6 us and backward 103.8 us, level with the
+// unclamped kernels, against 81.9 / 118.9 us with a balanced grid of 1920
+// resident-sized workgroups, whose last dispatch round ran half empty. Without the
+// clamp the kernel is a plain stream and follows the default grid rule.
 constexpr int kSquaredReluClampMaxU = MOE_SQRELU_CLAMP_MAX_U;
 
 // Under the clamp: at most 2 octs per lane per chunk (fewer registers, more waves).

@@ -214,6 +214,7 @@ __global__ __launch_bounds__(kBlock) void residual_add_kernel(const char *e, con
 // ---------------------------------------------------------------------------
 template <int XDT, int ODT, int U>
 struct RouterFwdOp {
+    static constexpr bool kRowSum = false;
     struct Buf {
         Oct x[U];
     };
@@ -255,11 +256,12 @@ __global__ __launch_bounds__(kBlock) void router_weight_fwd_kernel(const char *x
     const RowSchedule sched = make_schedule(tokens, nullptr, 0);
     const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
     RouterFwdOp<XDT, ODT, U> op{x, out, hidden, (uint32_t)lane_id()};
-    walk_rows(op, sched, nullptr, probs, nch);
+    walk_row_split(op, sched, nullptr, probs, nch);
 }
 
 template <int XDT, int ODT, int U>
 struct RouterBwdOp {
+    static constexpr bool kRowSum = true;
     struct Buf {
         Oct g[U], x[U];
     };
@@ -290,8 +292,6 @@ struct RouterBwdOp {
         const uint32_t xrow = (uint32_t)hidden * kElemBytes<XDT>;
         const rsrc_t rgx = chunk_rsrc(gx + r * xrow, slot >= 0 && gx ? xrow : 0u,
                                       (uint32_t)c * U * kWave * kOctBytes<XDT>);
-        if (c == 0)
-            acc = 0.0f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float fg[8], fx[8], d[8];
@@ -304,11 +304,13 @@ struct RouterBwdOp {
             }
             store_oct<XDT>(rgx, narrow<XDT>(d), (lane + u * kWave) * kOctBytes<XDT>);
         }
-        if (c == nch - 1 && slot >= 0 && gp) {
-            const float total = wave_sum(acc);
-            if (lane == 0)
-                gp[slot] = total;
-        }
+    }
+
+    __device__ __forceinline__ bool row_sum_wanted() const { return gp != nullptr; }
+    __device__ __forceinline__ void store_row_sum(int slot, float total) const
+    {
+        if (lane == 0)
+            gp[slot] = total;
     }
 };
 
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kBlock) void router_weight_bwd_kernel(const char *g
     const RowSchedule sched = make_schedule(tokens, nullptr, 0);
     const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
     RouterBwdOp<XDT, ODT, U> op{g, x, gx, gp, hidden, nch, (uint32_t)lane_id(), 0.0f};
-    walk_rows(op, sched, nullptr, probs, nch);
+    walk_row_split(op, sched, nullptr, probs, nch);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,6 +357,7 @@ __device__ __forceinline__ float soft_clamp_relu(float x, float s, float inv_s)
 
 template <int U, bool kClamp>
 struct SquaredReluOp {
+    static constexpr bool kRowSum = false;
     struct Buf {
         u32x4 x[U];
     };
@@ -432,6 +435,7 @@ __global__ __launch_bounds__(kBlock) void squared_relu_probs_kernel(
 // first (z = max(x / s, 0), NaN kept), so only z >= 0 is ever evaluated.
 template <int U, bool kClamp>
 struct SquaredReluBwdOp {
+    static constexpr bool kRowSum = true;
     struct Buf {
         u32x4 x[U], g[U];
     };
@@ -503,8 +507,6 @@ struct SquaredReluBwdOp {
         const uint32_t row = (uint32_t)hidden * 2u;
         const rsrc_t rgx = chunk_rsrc(gx + r * hidden, (slot >= 0 || zero_padding) ? row : 0u,
                                       (uint32_t)c * U * kWave * kVecBytes);
-        if (c == 0)
-            acc = 0.0f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             u32x4 o;
@@ -513,11 +515,13 @@ struct SquaredReluBwdOp {
                 o[q] = pair(b.x[u][q], b.g[u][q], p);
             store_vec(rgx, o, voff + u * kWave * kVecBytes);
         }
-        if (c == nch - 1 && slot >= 0 && gp) {
-            const float total = wave_sum(acc);
-            if (lane_id() == 0)
-                gp[slot] = total;
-        }
+    }
+
+    __device__ __forceinline__ bool row_sum_wanted() const { return gp != nullptr; }
+    __device__ __forceinline__ void store_row_sum(int slot, float total) const
+    {
+        if (lane_id() == 0)
+            gp[slot] = total;
     }
 };
 
@@ -1034,7 +1038,8 @@ moe_status_t moe_router_weight_fwd(const void *x, moe_dtype_t x_dtype, const flo
     if (he != hipSuccess)
         return fail_hip(he);
     const int U = pick_u(hidden / 8);
-    const int blocks = num_workgroups > 0 ? num_workgroups : walk_workgroups(tokens, row_chunks(hidden / 8, U), cus, 1);
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : split_walk_workgroups(tokens, row_chunks(hidden / 8, U), cus, 1);
     const int t = (int)tokens, h = (int)hidden;
     if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_BF16>(U, blocks, stream, x, probs, out, t, h);
     else if (x_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_F32>(U, blocks, stream, x, probs, out, t, h);
@@ -1078,7 +1083,8 @@ moe_status_t moe_router_weight_bwd(const void *grad_out, moe_dtype_t out_dtype, 
     if (he != hipSuccess)
         return fail_hip(he);
     const int U = pick_u(hidden / 8);
-    const int blocks = num_workgroups > 0 ? num_workgroups : walk_workgroups(tokens, row_chunks(hidden / 8, U), cus, 1);
+    const int blocks = num_workgroups > 0 ? num_workgroups
+                                          : split_walk_workgroups(tokens, row_chunks(hidden / 8, U), cus, 1);
     const int t = (int)tokens, h = (int)hidden;
     if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_BF16>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
     else if (x_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);

@@ -56,6 +56,9 @@ using namespace cdna4;
 #define SWIGLU_MAX_U 4
 #endif
 constexpr int kMaxU = SWIGLU_MAX_U;  // 16-byte vectors per lane per stream per chunk
+#ifndef SWIGLU_WALK
+#define SWIGLU_WALK walk_row_split
+#endif
 constexpr float kNegLog2e = -1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -114,6 +117,7 @@ __device__ __forceinline__ void bwd_elem(float a, float b, float g, float p, flo
 // ---------------------------------------------------------------------------
 template <int U>
 struct FwdOp {
+    static constexpr bool kRowSum = false;
     struct Buf {
         u32x4 g[U], u[U];
     };
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
     const int vpr = inter / 8;
     const int nch = (vpr + U * kWave - 1) / (U * kWave);
     FwdOp<U> op{x, y, inter, L, zero_padding, (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes};
-    walk_rows(op, sched, perm, probs, nch);
+    SWIGLU_WALK(op, sched, perm, probs, nch);
 }
 
 // ---------------------------------------------------------------------------
@@ -173,6 +177,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
 // ---------------------------------------------------------------------------
 template <int U>
 struct BwdOp {
+    static constexpr bool kRowSum = true;
     struct Buf {
         u32x4 g[U], u[U], d[U];
     };
@@ -208,8 +213,6 @@ struct BwdOp {
         uint16_t *dgate = gx + r * 2 * inter;
         const uint32_t off = (uint32_t)c * U * kWave * kVecBytes;
         const rsrc_t rdg = chunk_rsrc(dgate, n, off), rdu = chunk_rsrc(dgate + inter, n, off);
-        if (c == 0)
-            acc = 0.0f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             u32x4 og, ou;
@@ -224,11 +227,13 @@ struct BwdOp {
             store_vec(rdg, og, voff + u * kWave * kVecBytes);
             store_vec(rdu, ou, voff + u * kWave * kVecBytes);
         }
-        if (c == nch - 1 && slot >= 0 && gprobs) {
-            const float total = wave_sum(acc);
-            if ((threadIdx.x & (kWave - 1)) == 0)
-                gprobs[slot] = total;
-        }
+    }
+
+    __device__ __forceinline__ bool row_sum_wanted() const { return gprobs != nullptr; }
+    __device__ __forceinline__ void store_row_sum(int slot, float total) const
+    {
+        if (lane_id() == 0)
+            gprobs[slot] = total;
     }
 };
 
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_kernel(
     const int nch = (vpr + U * kWave - 1) / (U * kWave);
     BwdOp<U> op{x, gy, gx, gprobs, inter, nch, L, zero_padding,
                 (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes, 0.0f};
-    walk_rows(op, sched, perm, probs, nch);
+    SWIGLU_WALK(op, sched, perm, probs, nch);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,8 +424,8 @@ swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint1
     const int vpr = (int)(inter / 8);
     const int U = pick_u(vpr);
     const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
-                                                            info->fwd_blocks_per_cu[U]);
+                                          : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
+                                                                  info->fwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
     switch (U) {
     case 1: launch_fwd<1>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
@@ -468,8 +473,8 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
     const int vpr = (int)(inter / 8);
     const int U = pick_u(vpr);
     const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
-                                                            info->bwd_blocks_per_cu[U]);
+                                          : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
+                                                                  info->bwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
     switch (U) {
     case 1: launch_bwd<1>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
@@ -511,7 +516,7 @@ int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter)
         return -1;
     const int U = pick_u(inter / 8);
     const int bpc = direction == 0 ? info->fwd_blocks_per_cu[U] : info->bwd_blocks_per_cu[U];
-    return walk_workgroups(rows, chunks_per_row(inter / 8, U), info->cus, bpc);
+    return split_walk_workgroups(rows, chunks_per_row(inter / 8, U), info->cus, bpc);
 }
 
 const char *swiglu_probs_status_string(swiglu_status_t status)

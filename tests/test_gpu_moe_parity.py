@@ -120,6 +120,45 @@ def test_router_weight(x_dt, out_dt, tokens, hidden):
     assert bad.size == 0, f"router grad_probs: {bad.size} rows off"
 
 
+@pytest.mark.parametrize("hidden", [5120, 7168, 8192])
+def test_router_weight_rows_split_over_waves(hidden):
+    """Rows of 4 or more column chunks are shared by a workgroup's four waves (5, 7 and 4
+    chunks here): the probability gradient adds the waves' partials in wave order, so
+    every grid gives the same bits; outputs requested alone take the same paths."""
+    rng = np.random.default_rng(hidden)
+    tokens = 777
+    x = _rand((tokens, hidden), "bf16", rng, 3.0, specials=False)
+    g = _rand((tokens, hidden), "bf16", rng, 1.0, specials=False)
+    p = rng.uniform(0, 1, tokens).astype(np.float32)
+    orc = moe_oracle.get()
+    ref = orc.router_weight_bwd(g, "bf16", x, "bf16", p)
+    want_y = orc.router_weight_fwd(x, "bf16", p, "bf16")
+    xd, gd, dp = _dev(x, "bf16"), _dev(g, "bf16"), torch.from_numpy(p).to(DEV)
+    first = None
+    for nwg in (0, 1, 2, 3, 777, 1024):
+        y = torch.empty((tokens, hidden), dtype=torch.bfloat16, device=DEV)
+        gx = torch.empty_like(y)
+        gp = torch.full((tokens,), -7.0, device=DEV)
+        moe_router_weight_fwd(xd, dp, y, num_workgroups=nwg)
+        moe_router_weight_bwd(gd, xd, dp, gx, gp, num_workgroups=nwg)
+        torch.cuda.synchronize()
+        got = (_host(y, "bf16"), _host(gx, "bf16"), gp.cpu().numpy())
+        if first is None:
+            first = got
+            assert _same(got[0], want_y, "bf16") and _same(got[1], ref["grad_x"], "bf16")
+            assert grad_probs_violations(got[2], ref["grad_probs_f64"], ref["row_scale"]).size == 0
+        else:
+            assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1]), f"grid {nwg}"
+            assert np.array_equal(got[2].view(np.uint32), first[2].view(np.uint32)), f"grid {nwg}: grad_probs bits"
+    gp_only = torch.empty(tokens, device=DEV)
+    moe_router_weight_bwd(gd, xd, dp, None, gp_only)
+    gx_only = torch.empty((tokens, hidden), dtype=torch.bfloat16, device=DEV)
+    moe_router_weight_bwd(gd, None, dp, gx_only, None, x_dtype="bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(gp_only.cpu().numpy().view(np.uint32), first[2].view(np.uint32))
+    assert np.array_equal(_host(gx_only, "bf16"), first[1])
+
+
 def test_router_weight_optional_outputs():
     rng = np.random.default_rng(9)
     x = _rand((100, 512), "bf16", rng, specials=False)

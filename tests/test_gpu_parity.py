@@ -90,16 +90,20 @@ def test_dummy_map_entries(zero_padding):
 
 
 def test_default_workgroups():
-    """Rows of at most two column chunks: one wave per row. Longer rows: at most one
-    workgroup per CU, with no round of rows left mostly idle."""
+    """Rows of at most two column chunks: one wave per row. Three chunks: at most one
+    workgroup per CU, with no round of rows left mostly idle. Four or more: one workgroup
+    per row, its four waves sharing the row's chunks."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = WORKLOADS["headline"].rows
     for d in ("fwd", "bwd"):
-        wg = swiglu_probs_default_workgroups(d, rows, WORKLOADS["headline"].inter)
+        wg = swiglu_probs_default_workgroups(d, rows, WORKLOADS["headline"].inter)   # 1 chunk
         say(f"[launch] {d} inter {WORKLOADS['headline'].inter}: {wg} workgroups")
         assert wg == -(-rows // 4)
-        wg = swiglu_probs_default_workgroups(d, rows, 8192)      # 16 vectors per lane: 4 chunks
+        wg = swiglu_probs_default_workgroups(d, rows, 6144)      # 12 vectors per lane: 3 chunks
         waves = wg * 4
         rounds = -(-rows // waves)
-        say(f"[launch] {d} inter 8192: {wg} workgroups on {cus} CUs, {rounds} row rounds")
+        say(f"[launch] {d} inter 6144: {wg} workgroups on {cus} CUs, {rounds} row rounds")
         assert cus // 2 <= wg <= cus and rounds * waves - rows < waves
+        wg = swiglu_probs_default_workgroups(d, rows, 8192)      # 16 vectors per lane: 4 chunks
+        say(f"[launch] {d} inter 8192: {wg} workgroups")
+        assert wg == rows

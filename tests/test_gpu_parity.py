@@ -95,15 +95,19 @@ def test_default_workgroups():
     per row, its four waves sharing the row's chunks."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = WORKLOADS["headline"].rows
-    for d in ("fwd", "bwd"):
-        wg = swiglu_probs_default_workgroups(d, rows, WORKLOADS["headline"].inter)   # 1 chunk
-        say(f"[launch] {d} inter {WORKLOADS['headline'].inter}: {wg} workgroups")
-        assert wg == -(-rows // 4)
-        wg = swiglu_probs_default_workgroups(d, rows, 6144)      # 12 vectors per lane: 3 chunks
-        waves = wg * 4
-        rounds = -(-rows // waves)
-        say(f"[launch] {d} inter 6144: {wg} workgroups on {cus} CUs, {rounds} row rounds")
-        assert cus // 2 <= wg <= cus and rounds * waves - rows < waves
-        wg = swiglu_probs_default_workgroups(d, rows, 8192)      # 16 vectors per lane: 4 chunks
-        say(f"[launch] {d} inter 8192: {wg} workgroups")
+    # forward: pick_u's width; 2048 columns = 1 chunk, 6144 = 3 chunks, 8192 = 4 chunks
+    wg = swiglu_probs_default_workgroups("fwd", rows, WORKLOADS["headline"].inter)
+    say(f"[launch] fwd inter {WORKLOADS['headline'].inter}: {wg} workgroups")
+    assert wg == -(-rows // 4)
+    wg = swiglu_probs_default_workgroups("fwd", rows, 6144)
+    waves = wg * 4
+    rounds = -(-rows // waves)
+    say(f"[launch] fwd inter 6144: {wg} workgroups on {cus} CUs, {rounds} row rounds")
+    assert cus // 2 <= wg <= cus and rounds * waves - rows < waves
+    assert swiglu_probs_default_workgroups("fwd", rows, 8192) == rows
+    # backward: rows of 4 or more vectors per lane are shared by the four waves
+    for inter in (2048, 6144, 8192):
+        wg = swiglu_probs_default_workgroups("bwd", rows, inter)
+        say(f"[launch] bwd inter {inter}: {wg} workgroups")
         assert wg == rows
+    assert swiglu_probs_default_workgroups("bwd", rows, 1536) == -(-rows // 4)   # 3 vectors per lane

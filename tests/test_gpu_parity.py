@@ -89,6 +89,28 @@ def test_dummy_map_entries(zero_padding):
     check_parity(inp, label=f"dummy entries zero_padding={zero_padding}")
 
 
+@pytest.mark.parametrize("inter", [2048, 4096])
+@pytest.mark.parametrize("zero_padding", [False, True])
+def test_row_bookkeeping_on_shared_rows(inter, zero_padding):
+    """The backward shares these rows among a workgroup's four waves (a barrier per row
+    with a slot): device n_used, a permutation with interior dummy entries, and padding
+    rows must behave as on whole-row walks."""
+    from memory_bound_elementwise_amd.workloads import Workload
+    rows = 3001
+    w = Workload("shared", rows=rows, inter=inter, limit=7.0, x_std=3.0, probs="topk_softmax",
+                 n_used=2500, permute=True, zero_padding=zero_padding)
+    inp = make_inputs(w, seed=inter + zero_padding)
+    pm = inp["permutation_map"].copy()
+    rng = np.random.default_rng(inter)
+    dummy = rng.choice(2500, size=60, replace=False)
+    pm[dummy[:30]] = -1
+    pm[dummy[30:]] = rows + rng.integers(0, 100, size=30)
+    inp["permutation_map"] = pm
+    for n_used in (2500, 1, 0):
+        inp["n_used"] = n_used
+        check_parity(inp, label=f"shared rows inter={inter} zp={zero_padding} n_used={n_used}")
+
+
 def test_default_workgroups():
     """Rows of at most two column chunks: one wave per row. Three chunks: at most one
     workgroup per CU, with no round of rows left mostly idle. Four or more: one workgroup

@@ -4,16 +4,20 @@
 //   residual add   Megatron-Core "core.fusions.fused_moe_residual_add" page
 //   router weight  NeMo AutoModel "moe/optimized_ops" page (_RouterWeightMulFunction)
 //   squared ReLU   Megatron-Core "core.inference.moe.batch_invariant" page
-//                  (_squared_relu_with_probs_kernel, squared_relu_with_probs)
+//                  (_squared_relu_with_probs_kernel, squared_relu_with_probs);
+//                  the backward is the chain rule through it (the page gives none)
 //   unpermute      same page (_unpermute_tokens_in_expert_order_kernel)
 //
-// All four are HBM-bound streams built on cdna4_stream.h: 128-bit buffer accesses
-// on per-row (or per-block) resources whose hardware range check masks ragged ends
-// and rows that are not live, nontemporal hints, and (residual add, router weight,
-// squared ReLU) the two-buffer software pipeline per wave. The pure streams launch
-// one workgroup per CU; the soft-clamped squared ReLU (arithmetic-heavy) and the
-// unpermute (gather-latency-bound) keep two per CU resident. Values are handled in groups of eight
-// elements per lane ("octs": one 16-byte access for 16-bit types, two for fp32).
+// All are streams built on cdna4_stream.h: 128-bit buffer accesses on per-row (or
+// per-block) resources whose hardware range check masks ragged ends and rows that
+// are not live, nontemporal hints, and the two-buffer software pipeline per wave.
+// Grids follow the shared rules (walk_workgroups / split_walk_workgroups): one wave
+// per row or 4 KiB block for short rows, rows of 4 or more chunks shared by a
+// workgroup's four waves (router weight), one persistent workgroup per CU for the
+// pipelined unpermute. The soft-clamped squared ReLU, the one op the vector ALU
+// rather than HBM bounds, always runs one wave per row. Values are handled in groups
+// of eight elements per lane ("octs": one 16-byte access for 16-bit types, two for
+// fp32).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>

@@ -11,10 +11,12 @@
 //   _weighted_silu_mul_bounded_kernel).
 //
 // Design (HBM-bound; no MFMA):
-//   * One wavefront (64 lanes) owns one row at a time. Lane l handles the 16-byte
-//     vectors l, l+64, l+128, ... of the gate half, the up half and (backward)
-//     grad_y: every access is 128 bits wide and one wave instruction covers 1 KiB
-//     of contiguous memory. A row is processed in chunks of U vectors per lane.
+//   * Lane l of a wave handles the 16-byte vectors l, l+64, l+128, ... of the gate
+//     half, the up half and (backward) grad_y: every access is 128 bits wide and one
+//     wave instruction covers 1 KiB of contiguous memory. A row is processed in
+//     chunks of U vectors per lane. The forward gives each wave whole rows; the
+//     backward shares rows of 4 or more vectors per lane among a workgroup's four
+//     waves, a quarter of the chunks each (walk_rows / walk_row_split).
 //   * Every load and store is a buffer instruction on a per-row buffer resource
 //     whose size is the row's byte length, or 0 for a row that is not live. The
 //     hardware range check then does all masking: lanes past the row end and rows
@@ -25,16 +27,19 @@
 //   * Software pipeline: each wave holds two register buffers and issues the loads
 //     of its next chunk (usually its next row) before computing the current one,
 //     so its own memory traffic overlaps its arithmetic.
-//   * Waves stride over rows with a fixed grid (row r, r + W, r + 2W, ...), so the
-//     launch never depends on device data and is graph-safe; the host sizes the
-//     grid so every wave gets the same number of rows.
+//   * Waves (or workgroups, for shared rows) stride over rows with a fixed grid
+//     (row r, r + W, r + 2W, ...), so the launch never depends on device data and
+//     is graph-safe. By default the grid has one wave (or workgroup) per row; rows
+//     of exactly three chunks get one persistent workgroup per CU instead, sized so
+//     every wave gets the same number of rows (walk_workgroups in cdna4_stream.h).
 //   * Per-row metadata (permutation slot and probability) for a wave's next 64
 //     rows is gathered with one vector load, one row per lane, and broadcast with
 //     v_readlane when the row is processed: no per-row dependent scalar loads.
 //   * The probability gradient: each lane sums its own columns in a fixed order,
 //     then a butterfly over the wave (DPP quad/row permutes, then two lane
-//     exchanges) combines the 64 partials. The order depends only on the column to
-//     lane mapping, never on the grid, so the bits are grid-invariant.
+//     exchanges) combines the 64 partials; on shared rows the four waves' totals
+//     are then added in wave order through LDS. The order depends only on the row
+//     width, never on the grid, so the bits are grid-invariant.
 //   * fp32 -> bf16 uses v_cvt_pk_bf16_f32 (round to nearest even, two values per
 //     instruction); the clamps use v_minimum3/v_maximum3 (NaN-propagating, as
 //     torch.clamp); the inclusive masks are "the clamp left the value unchanged".

@@ -8,8 +8,9 @@ bracketed by device synchronisation.
 
 Printed JSON line (stdout):
   value        whole-job algorithmic GB/s = (fwd + bwd algorithmic bytes) / step time
-  fwd, bwd     per-kernel average duration from HIP events recorded around every
-               launch on the launch stream, and the GB/s and HBM fraction they give
+  fwd, bwd     per-kernel average duration from HIP events on the launch stream,
+               one before the first launch and one after every launch (each launch
+               lies between two), and the GB/s and HBM fraction they give
   roofline     for the dominant kernel (the backward): algorithmic bytes per launch /
                its average duration, against the 8 TB/s MI355X HBM peak; traffic =
                HBM bytes per launch from the committed rocprofv3 counter summary when
@@ -96,24 +97,34 @@ MOE_OPS = {
 
 
 def time_kernels(kernels, steps, warmup, cold_reps):
-    """kernels: list of (name, launch). Returns wall ms per step, per-kernel event
-    times (lists, ms) over the timed steps, and cold medians (ms) per kernel."""
+    """kernels: list of (name, launch), one step being each launched once in order.
+    Returns wall ms per step, per-kernel event times (lists, ms) over the timed steps,
+    and cold medians (ms) per kernel (empty when cold_reps is 0).
+
+    One event is recorded before the first launch and one after every launch, on the
+    launch stream, so each launch lies between two events and consecutive launches
+    share the one between them. Each recorded event costs the stream a few
+    microseconds (measured on MI355X: 2 events per fwd+bwd step instead of 3 took the
+    step from 283 to 278 us; with none it is 272 us), so no more are recorded than
+    the per-launch durations need."""
     import numpy as np
     import torch
     for _ in range(warmup):
         for _, fn in kernels:
             fn()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(steps)]
+    n = len(kernels)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * n + 1)]
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record()
+    ev[0].record()
+    for s in range(steps):
         for i, (_, fn) in enumerate(kernels):
             fn()
-            e[i + 1].record()
+            ev[s * n + i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, (name, _) in enumerate(kernels)}
+    per = {name: [ev[s * n + i].elapsed_time(ev[s * n + i + 1]) for s in range(steps)]
+           for i, (name, _) in enumerate(kernels)}
     cold = {}
     if cold_reps > 0:
         evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
@@ -251,7 +262,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="headline",
                     choices=["tiny", "mid", "headline", "padded", "edge"])
     ap.add_argument("--op", default="swiglu_probs", choices=["swiglu_probs"] + sorted(MOE_OPS),
@@ -305,32 +316,13 @@ def main() -> int:
     fwd_bytes = algorithmic_bytes(w, "fwd")
     bwd_bytes = algorithmic_bytes(w, "bwd")
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        swiglu_probs_fwd(x, probs, y, L, num_workgroups=args.fwd_workgroups, **kw)
-        if ev is not None:
-            ev[1].record()
-        swiglu_probs_bwd(x, probs, gy, gx, gp, L, num_workgroups=args.bwd_workgroups, **kw)
-        if ev is not None:
-            ev[2].record()
-
-    log(f"warm-up {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
-    ms_per_step = wall * 1e3 / args.steps
+    kernels = [
+        ("fwd", lambda: swiglu_probs_fwd(x, probs, y, L, num_workgroups=args.fwd_workgroups, **kw)),
+        ("bwd", lambda: swiglu_probs_bwd(x, probs, gy, gx, gp, L, num_workgroups=args.bwd_workgroups, **kw)),
+    ]
+    log(f"warm-up {args.warmup} steps, timing {args.steps} steps")
+    ms_per_step, per, cold_ms = time_kernels(kernels, args.steps, args.warmup, args.cold_reps)
+    fwd_ms, bwd_ms = per["fwd"], per["bwd"]
     f_avg, b_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
     f_gbs, b_gbs = fwd_bytes / (f_avg * 1e6), bwd_bytes / (b_avg * 1e6)
     value = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e6)
@@ -339,24 +331,7 @@ def main() -> int:
 
     cold = None
     if args.cold_reps > 0:
-        log(f"cold: {args.cold_reps} launches of each kernel after a 1 GiB read")
-        evict = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        cf, cb = [], []
-        for _ in range(args.cold_reps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            evict.sum(dtype=torch.int64)
-            ev[0].record()
-            swiglu_probs_fwd(x, probs, y, L, num_workgroups=args.fwd_workgroups, **kw)
-            ev[1].record()
-            evict.sum(dtype=torch.int64)
-            ev[2].record()
-            swiglu_probs_bwd(x, probs, gy, gx, gp, L, num_workgroups=args.bwd_workgroups, **kw)
-            ev[3].record()
-            torch.cuda.synchronize()
-            cf.append(ev[0].elapsed_time(ev[1]))
-            cb.append(ev[2].elapsed_time(ev[3]))
-        del evict
-        cfm, cbm = float(np.median(cf)), float(np.median(cb))
+        cfm, cbm = cold_ms["fwd"], cold_ms["bwd"]
         cold = {"fwd_us": round(cfm * 1e3, 2), "fwd_GB/s": round(fwd_bytes / (cfm * 1e6), 1),
                 "bwd_us": round(cbm * 1e3, 2), "bwd_GB/s": round(bwd_bytes / (cbm * 1e6), 1),
                 "reps": args.cold_reps, "statistic": "median"}

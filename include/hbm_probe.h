@@ -12,8 +12,9 @@
  *
  * Pointers: device memory on the current HIP device, 16-byte aligned, caller-owned,
  * destinations must not overlap sources. 1 <= n_src <= 3, 1 <= n_dst <= 2.
- * num_workgroups = 0 launches one wave per 4 KiB block, the activation kernels'
- * default grid for short rows. Accesses are 128-bit buffer loads/stores with the
+ * num_workgroups = 0 launches one wave per 4 KiB block (at most 16,777,215
+ * workgroups), the activation kernels' default grid for short rows; an explicit
+ * count must not exceed 16,777,215. Accesses are 128-bit buffer loads/stores with the
  * nontemporal hint, pipelined like the activation kernels, without their arithmetic. Work is enqueued on
  * `stream`; no synchronisation, no allocation.
  * Returns 0 on success, 1 for invalid arguments, 3 when the launch failed.

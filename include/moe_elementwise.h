@@ -21,9 +21,14 @@
  *     allocation, no host read of device data: calls are hipGraph-capturable.
  *   - Arguments are checked on the host before anything is launched; on error nothing
  *     is written.
- *   - num_workgroups: 0 = the library's choice (one wave per row or block when a row
- *     is at most two column chunks, else one workgroup per CU with the rows balanced
- *     over the waves); any positive count gives the same result bits.
+ *   - num_workgroups: 0 = the library's choice: one wave per row or block when a row
+ *     is at most two column chunks (and always for the soft-clamped squared ReLU);
+ *     one workgroup per row, its four waves sharing the row, for router-weight rows
+ *     of four or more chunks; else persistent workgroups (one per CU) with the rows
+ *     balanced over the waves. Never more than 16,777,215 workgroups (a dispatch
+ *     holds its work-item count in 32 bits); the waves then take several rows each.
+ *     An explicit count must lie in 1 .. 16,777,215; any count gives the same
+ *     result bits.
  *   - The library keeps no pointer after a call returns; calls are thread-safe.
  */
 #ifndef MOE_ELEMENTWISE_H
@@ -42,7 +47,8 @@ typedef enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype_t;
 
 typedef enum moe_status {
     MOE_OK = 0,
-    MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, dtype or scale, overlap */
+    MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, dtype, scale or
+                                 workgroup count, overlap */
     MOE_ERR_ALIGNMENT = 2,    /* misaligned pointer, or a row width not a multiple of 8 */
     MOE_ERR_HIP = 3           /* launch failed; see moe_elementwise_last_hip_error */
 } moe_status_t;

@@ -63,7 +63,8 @@ extern "C" {
 typedef enum swiglu_status {
     SWIGLU_OK = 0,
     /* a required pointer is NULL, rows < 0, inter <= 0, rows or inter too large,
-     * limit is NaN or <= 0, num_workgroups < 0, or an output overlaps an input */
+     * limit is NaN or <= 0, num_workgroups < 0 or > 16,777,215, or an output
+     * overlaps an input */
     SWIGLU_ERR_INVALID_ARG = 1,
     /* inter % 8 != 0, or a base pointer misses its alignment (16 B for bf16
      * tensors, 4 B for fp32/int32) */
@@ -124,8 +125,13 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
 
 /* Workgroup count the library would launch for this call shape on the current
  * device (direction 0 = forward, 1 = backward), or -1 on error. Host only.
- * Rows of at most two column chunks (inter <= 4096 for bf16) get one wave per row,
- * ceil(rows / 4) workgroups; longer rows one workgroup per CU, balanced. */
+ * A row is cut into column chunks of U 16-byte vectors per lane (64 lanes): the
+ * forward takes the U in 1..4 that leaves the fewest idle lanes, the backward cuts
+ * rows of 4 or more vectors per lane into 4 or more chunks. Rows of one or two
+ * chunks get one wave per row, ceil(rows / 4) workgroups; rows of three chunks one
+ * workgroup per CU, balanced; rows of four or more one workgroup per row, its four
+ * waves sharing the row. Never more than 16,777,215 workgroups (a dispatch holds
+ * its work-item count in 32 bits); the waves then take several rows each. */
 int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter);
 
 /* Static text for a status code. Never NULL. */

@@ -385,10 +385,18 @@ inline int balanced_workgroups(int64_t units, int cus, int resident_blocks_per_c
     return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
+// A dispatch packet holds the grid size in work-items as a 32-bit count, so a launch of
+// kBlock-thread workgroups has at most this many. The walks stride over whatever the
+// grid does not cover, so a capped grid gives the same result bits.
+constexpr int kMaxWorkgroups = (int)(0xffffffffu / kBlock);  // 16,777,215
+
+inline int cap_workgroups(int64_t n) { return n > kMaxWorkgroups ? kMaxWorkgroups : (int)n; }
+
 // Default grid of a walk over `units` rows (or blocks) of `chunks` chunks each.
-//   * Units of one or two chunks: one wave per unit, ceil(units / 4) workgroups, which
-//     the dispatcher starts as slots free up. The rows in flight then stay one
-//     contiguous window of the arrays. Measured on MI355X at 53760 x 2048: activation
+//   * Units of one or two chunks: one wave per unit, ceil(units / 4) workgroups (at
+//     most kMaxWorkgroups), which the dispatcher starts as slots free up. The rows in
+//     flight then stay one contiguous window of the arrays. Measured on MI355X at
+//     53760 x 2048: activation
 //     forward 6.38 and backward 6.28 TB/s, against 6.10 / 5.76 TB/s with one persistent
 //     workgroup per CU; the plain streaming probe gains alike (2:1 6.26 -> 6.50, 3:2
 //     6.15 -> 6.31 TB/s). Grids of 4 to 16 persistent workgroups per CU were slower
@@ -404,20 +412,20 @@ inline int walk_workgroups(int64_t units, int64_t chunks, int cus, int resident_
     if (units <= 0)
         return 1;
     if (chunks <= kPerWaveMaxChunks)
-        return (int)((units + kWavesPerBlock - 1) / kWavesPerBlock);
+        return cap_workgroups((units + kWavesPerBlock - 1) / kWavesPerBlock);
     return balanced_workgroups(units, cus, resident_blocks_per_cu);
 }
 
-// Default grid of walk_row_split: one workgroup per row when the four waves share it
-// (at least 4 chunks), else the walk_rows grid above. For the 7168-column MoE router
-// rows this measured 6.19 / 6.28 TB/s (forward / backward) against 5.79 / 5.87 with one
-// persistent workgroup per CU walking whole rows per wave.
+// Default grid of walk_row_split: one workgroup per row (at most kMaxWorkgroups) when
+// the four waves share it (at least 4 chunks), else the walk_rows grid above. For the
+// 7168-column MoE router rows this measured 6.19 / 6.28 TB/s (forward / backward)
+// against 5.79 / 5.87 with one persistent workgroup per CU walking whole rows per wave.
 inline int split_walk_workgroups(int64_t units, int64_t chunks, int cus, int resident_blocks_per_cu)
 {
     if (units <= 0)
         return 1;
     if (chunks >= kWavesPerBlock)
-        return units > 0x7fffffff ? 0x7fffffff : (int)units;
+        return cap_workgroups(units);
     return walk_workgroups(units, chunks, cus, resident_blocks_per_cu);
 }
 

@@ -103,7 +103,7 @@ extern "C" int hbm_probe_stream(const void *const *src, int n_src, void *const *
                                 int64_t n_vec, int num_workgroups, hipStream_t stream)
 {
     if (!src || !dst || n_src < 1 || n_src > 3 || n_dst < 1 || n_dst > 2 || n_vec < 0 ||
-        num_workgroups < 0)
+        num_workgroups < 0 || num_workgroups > kMaxWorkgroups)
         return 1;
     if (n_vec == 0)
         return 0;

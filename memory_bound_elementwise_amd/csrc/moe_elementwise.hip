@@ -274,7 +274,6 @@ struct RouterBwdOp {
     char *gx;
     float *gp;
     int hidden;
-    int nch;
     uint32_t lane;
     float acc;  // this lane's partial of the current row's probability gradient
 
@@ -325,7 +324,7 @@ __global__ __launch_bounds__(kBlock) void router_weight_bwd_kernel(const char *g
 {
     const RowSchedule sched = make_schedule(tokens, nullptr, 0);
     const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
-    RouterBwdOp<XDT, ODT, U> op{g, x, gx, gp, hidden, nch, (uint32_t)lane_id(), 0.0f};
+    RouterBwdOp<XDT, ODT, U> op{g, x, gx, gp, hidden, (uint32_t)lane_id(), 0.0f};
     walk_row_split(op, sched, nullptr, probs, nch);
 }
 
@@ -448,7 +447,6 @@ struct SquaredReluBwdOp {
     uint16_t *gx;
     float *gp;
     int hidden;
-    int nch;
     float s, inv_s;
     int zero_padding;
     uint32_t voff;
@@ -536,7 +534,7 @@ __global__ __launch_bounds__(kBlock) void squared_relu_probs_bwd_kernel(
 {
     const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
     const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
-    SquaredReluBwdOp<U, kClamp> op{x, g, gx, gp, hidden, nch, s, inv_s, zero_padding,
+    SquaredReluBwdOp<U, kClamp> op{x, g, gx, gp, hidden, s, inv_s, zero_padding,
                                    (uint32_t)lane_id() * kVecBytes, 0.0f};
     walk_rows(op, sched, perm, probs, nch);
 }
@@ -954,13 +952,16 @@ constexpr int kUnpermutePipelinedMaxExperts = MOE_UNPERMUTE_PIPELINED ? 8 : 0;
 constexpr int kUnpermutePipeU = MOE_UNPERMUTE_PIPE_U;
 constexpr int kUnpermutePipeBlocksPerCU = MOE_UNPERMUTE_PIPE_BPC;
 // The soft-clamped squared ReLU (forward ~19, backward ~30 vector instructions per
-// element) keeps the VALU 78% / 90% busy. It runs with 2 octs per lane per chunk
+// element) keeps the VALU 74% / 86% busy. It runs with 2 octs per lane per chunk
 // (83 registers, up to 6 waves per SIMD) and one wave per row whatever the row length.
 // Measured at 53760 x 2048: forward 72.6 us and backward 103.8 us, level with the
 // unclamped kernels, against 81.9 / 118.9 us with a balanced grid of 1920
 // resident-sized workgroups, whose last dispatch round ran half empty. Without the
 // clamp the kernel is a plain stream and follows the default grid rule.
 constexpr int kSquaredReluClampMaxU = MOE_SQRELU_CLAMP_MAX_U;
+
+// An explicit workgroup count: 0 (the default grid) up to the dispatch limit.
+bool bad_grid(int num_workgroups) { return num_workgroups < 0 || num_workgroups > kMaxWorkgroups; }
 
 // Under the clamp: at most 2 octs per lane per chunk (fewer registers, more waves).
 int squared_relu_u(int64_t octs, int clamp)
@@ -989,7 +990,7 @@ moe_status_t moe_residual_add(const void *expert_output, const void *shared_expe
                               const void *residual, void *output, int64_t num_elements,
                               moe_dtype_t dtype, hipStream_t stream, int num_workgroups)
 {
-    if (num_elements < 0 || !dtype_ok(dtype) || num_workgroups < 0)
+    if (num_elements < 0 || !dtype_ok(dtype) || bad_grid(num_workgroups))
         return MOE_ERR_INVALID_ARG;
     if (num_elements == 0)
         return MOE_OK;
@@ -1022,7 +1023,7 @@ moe_status_t moe_router_weight_fwd(const void *x, moe_dtype_t x_dtype, const flo
                                    void *out, moe_dtype_t out_dtype, int64_t tokens,
                                    int64_t hidden, hipStream_t stream, int num_workgroups)
 {
-    if (tokens < 0 || hidden <= 0 || tokens > kMaxRows || hidden > kMaxHidden || num_workgroups < 0 ||
+    if (tokens < 0 || hidden <= 0 || tokens > kMaxRows || hidden > kMaxHidden || bad_grid(num_workgroups) ||
         !dtype_ok(x_dtype) || !(out_dtype == x_dtype || out_dtype == MOE_FP32))
         return MOE_ERR_INVALID_ARG;
     if (hidden % 8 != 0)
@@ -1058,7 +1059,7 @@ moe_status_t moe_router_weight_bwd(const void *grad_out, moe_dtype_t out_dtype, 
                                    float *grad_probs, int64_t tokens, int64_t hidden,
                                    hipStream_t stream, int num_workgroups)
 {
-    if (tokens < 0 || hidden <= 0 || tokens > kMaxRows || hidden > kMaxHidden || num_workgroups < 0 ||
+    if (tokens < 0 || hidden <= 0 || tokens > kMaxRows || hidden > kMaxHidden || bad_grid(num_workgroups) ||
         !dtype_ok(x_dtype) || !(out_dtype == x_dtype || out_dtype == MOE_FP32))
         return MOE_ERR_INVALID_ARG;
     if (hidden % 8 != 0)
@@ -1104,7 +1105,7 @@ moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, u
                                         const int32_t *permutation_map, int zero_padding,
                                         hipStream_t stream, int num_workgroups)
 {
-    if (rows < 0 || hidden <= 0 || rows > kMaxRows || hidden > kMaxHidden || num_workgroups < 0)
+    if (rows < 0 || hidden <= 0 || rows > kMaxRows || hidden > kMaxHidden || bad_grid(num_workgroups))
         return MOE_ERR_INVALID_ARG;
     if (clamp && !(clamp_scale > 0.0f && std::isfinite(clamp_scale)))
         return MOE_ERR_INVALID_ARG;
@@ -1145,7 +1146,7 @@ moe_status_t moe_squared_relu_probs_bwd(const uint16_t *x, const float *probs, c
                                         const int32_t *n_used, const int32_t *permutation_map,
                                         int zero_padding, hipStream_t stream, int num_workgroups)
 {
-    if (rows < 0 || hidden <= 0 || rows > kMaxRows || hidden > kMaxHidden || num_workgroups < 0)
+    if (rows < 0 || hidden <= 0 || rows > kMaxRows || hidden > kMaxHidden || bad_grid(num_workgroups))
         return MOE_ERR_INVALID_ARG;
     if (clamp && !(clamp_scale > 0.0f && std::isfinite(clamp_scale)))
         return MOE_ERR_INVALID_ARG;
@@ -1192,7 +1193,7 @@ moe_status_t moe_unpermute_expert_order(const uint16_t *expert_output, int64_t e
 {
     if (tokens < 0 || hidden <= 0 || expert_rows < 0 || tokens > kMaxRows || hidden > kMaxHidden ||
         expert_rows > kMaxRows || num_local_experts < 1 || num_local_experts > 1024 ||
-        num_workgroups < 0 || !(out_dtype == MOE_FP32 || out_dtype == MOE_BF16))
+        bad_grid(num_workgroups) || !(out_dtype == MOE_FP32 || out_dtype == MOE_BF16))
         return MOE_ERR_INVALID_ARG;
     if (hidden % 8 != 0)
         return MOE_ERR_ALIGNMENT;

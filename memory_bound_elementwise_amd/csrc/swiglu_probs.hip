@@ -14,9 +14,11 @@
 //   * Lane l of a wave handles the 16-byte vectors l, l+64, l+128, ... of the gate
 //     half, the up half and (backward) grad_y: every access is 128 bits wide and one
 //     wave instruction covers 1 KiB of contiguous memory. A row is processed in
-//     chunks of U vectors per lane. The forward gives each wave whole rows; the
-//     backward shares rows of 4 or more vectors per lane among a workgroup's four
-//     waves, a quarter of the chunks each (walk_rows / walk_row_split).
+//     chunks of U vectors per lane: the forward takes the U that leaves the fewest
+//     idle lanes, the backward cuts rows of 4 or more vectors per lane into 4 or more
+//     chunks. Rows of 4 or more chunks are shared by a workgroup's four waves, a
+//     quarter of the chunks each (walk_row_split); shorter rows go one per wave
+//     (walk_rows).
 //   * Every load and store is a buffer instruction on a per-row buffer resource
 //     whose size is the row's byte length, or 0 for a row that is not live. The
 //     hardware range check then does all masking: lanes past the row end and rows
@@ -29,9 +31,10 @@
 //     so its own memory traffic overlaps its arithmetic.
 //   * Waves (or workgroups, for shared rows) stride over rows with a fixed grid
 //     (row r, r + W, r + 2W, ...), so the launch never depends on device data and
-//     is graph-safe. By default the grid has one wave (or workgroup) per row; rows
-//     of exactly three chunks get one persistent workgroup per CU instead, sized so
-//     every wave gets the same number of rows (walk_workgroups in cdna4_stream.h).
+//     is graph-safe. By default the grid has one wave (or workgroup) per row, up to
+//     the dispatch limit of 16,777,215 workgroups; rows of exactly three chunks get
+//     one persistent workgroup per CU instead, sized so every wave gets the same
+//     number of rows (walk_workgroups in cdna4_stream.h).
 //   * Per-row metadata (permutation slot and probability) for a wave's next 64
 //     rows is gathered with one vector load, one row per lane, and broadcast with
 //     v_readlane when the row is processed: no per-row dependent scalar loads.
@@ -191,7 +194,6 @@ struct BwdOp {
     uint16_t *__restrict__ gx;
     float *__restrict__ gprobs;
     int inter;
-    int nch;
     float L;
     int zero_padding;
     uint32_t voff;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_kernel(
     const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
     const int vpr = inter / 8;
     const int nch = (vpr + U * kWave - 1) / (U * kWave);
-    BwdOp<U> op{x, gy, gx, gprobs, inter, nch, L, zero_padding,
+    BwdOp<U> op{x, gy, gx, gprobs, inter, L, zero_padding,
                 (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes, 0.0f};
     SWIGLU_WALK(op, sched, perm, probs, nch);
 }
@@ -375,7 +377,7 @@ swiglu_status_t check_shape(int64_t rows, int64_t inter, float limit, int num_wo
         return SWIGLU_ERR_INVALID_ARG;
     if (!(limit > 0.0f))  // NaN or <= 0; +inf is allowed (no clamp)
         return SWIGLU_ERR_INVALID_ARG;
-    if (num_workgroups < 0)
+    if (num_workgroups < 0 || num_workgroups > kMaxWorkgroups)
         return SWIGLU_ERR_INVALID_ARG;
     if (inter % 8 != 0)
         return SWIGLU_ERR_ALIGNMENT;

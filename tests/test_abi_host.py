@@ -86,6 +86,8 @@ def test_validation_fwd():
     assert fwd(lib, limit=0.0) == 1
     assert fwd(lib, limit=-7.0) == 1
     assert fwd(lib, nwg=-1) == 1
+    assert fwd(lib, nwg=1 << 24) == 1                   # past 2^32 - 1 work-items per dispatch
+    assert fwd(lib, nwg=2 ** 31 - 1) == 1
     assert fwd(lib, x=None) == 1
     assert fwd(lib, probs=None) == 1
     assert fwd(lib, y=None) == 1
@@ -105,6 +107,7 @@ def test_validation_bwd():
     assert bwd(lib, rows=0) == 0
     assert bwd(lib, rows=-3) == 1
     assert bwd(lib, inter=20) == 2
+    assert bwd(lib, nwg=1 << 24) == 1
     assert bwd(lib, limit=float("nan")) == 1
     assert bwd(lib, x=None) == 1
     assert bwd(lib, gy=None) == 1
@@ -140,6 +143,7 @@ def test_probe_validation(built):
     assert so.hbm_probe_stream(s, 1, d, 3, 4, 0, None) == 1
     d2 = (ctypes.c_void_p * 1)(A16 + 16)
     assert so.hbm_probe_stream(s, 1, d2, 1, 4, 0, None) == 1   # overlap
+    assert so.hbm_probe_stream(s, 1, d, 1, 4, 1 << 24, None) == 1
 
 
 def test_moe_validation():
@@ -152,20 +156,25 @@ def test_moe_validation():
     assert lib.moe_residual_add(a + 2, b, c, d, 8, 0, None, 0) == 2
     assert lib.moe_residual_add(a, b, c, a + 16, 64, 0, None, 0) == 1      # partial overlap
     assert lib.moe_residual_add(None, b, c, d, 8, 0, None, 0) == 1
+    assert lib.moe_residual_add(a, b, c, d, 8, 0, None, -1) == 1
+    assert lib.moe_residual_add(a, b, c, d, 8, 0, None, 1 << 24) == 1     # past the dispatch limit
     f = lib.moe_router_weight_fwd
     assert f(a, 0, b, c, 0, 0, 8, None, 0) == 0
     assert f(a, 0, b, c, 1, 4, 8, None, 0) == 1                           # out must be x's type or fp32
     assert f(a, 0, b, c, 2, 4, 12, None, 0) == 2                          # hidden % 8
     assert f(a, 0, b + 2, c, 2, 4, 8, None, 0) == 2
     assert f(a, 0, b, a, 0, 4, 8, None, 0) == 1                           # out over x
+    assert f(a, 0, b, c, 0, 4, 8, None, 1 << 24) == 1
     g = lib.moe_router_weight_bwd
     assert g(a, 0, None, 0, b, c, d, 4, 8, None, 0) == 1                  # grad_probs needs x
+    assert g(a, 0, A16 + (5 << 24), 0, b, c, d, 4, 8, None, 1 << 24) == 1
     sq = lib.moe_squared_relu_probs_fwd
     assert sq(a, b, c, 4, 8, 1, 0.0, None, None, 0, None, 0) == 1         # clamp needs scale > 0
     assert sq(a, b, c, 4, 8, 1, float("inf"), None, None, 0, None, 0) == 1
     assert sq(a, b, c, 4, 8, 1, float("nan"), None, None, 0, None, 0) == 1
     assert sq(a, b, c, 0, 8, 0, 0.0, None, None, 0, None, 0) == 0
     assert sq(a, b, a, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1
+    assert sq(a, b, c, 4, 8, 0, 0.0, None, None, 0, None, 1 << 24) == 1
     sb = lib.moe_squared_relu_probs_bwd
     e = A16 + (4 << 24)
     assert sb(a, b, c, d, e, 0, 8, 1, 2.0, None, None, 0, None, 0) == 0   # empty: no launch
@@ -180,12 +189,14 @@ def test_moe_validation():
     assert sb(a, b, c, d, b, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1       # grad_probs over probs
     assert sb(a, b, c, d, d + 16, 4, 8, 0, 0.0, None, None, 0, None, 0) == 1  # outputs overlap
     assert sb(a, b, c, d, e, 4, 8, 0, 0.0, d, None, 0, None, 0) == 1         # n_used under grad_x
+    assert sb(a, b, c, d, e, 4, 8, 0, 0.0, None, None, 0, None, 1 << 24) == 1
     u = lib.moe_unpermute_expert_order
     assert u(a, 10, b, None, c, 2, 0, 8, 4, None, 0) == 0
     assert u(a, 10, b, None, c, 1, 4, 8, 4, None, 0) == 1                 # fp16 out not supported
     assert u(a, 10, b, None, c, 2, 4, 8, 0, None, 0) == 1                 # no experts
     assert u(a, 10, b, None, c, 2, 4, 8, 2000, None, 0) == 1
     assert u(a, 10, b + 1, None, c, 2, 4, 8, 4, None, 0) == 2
+    assert u(a, 10, b, None, c, 2, 4, 8, 4, None, 1 << 24) == 1
     assert lib.moe_elementwise_abi_version() == 1
 
 

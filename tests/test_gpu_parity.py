@@ -114,7 +114,7 @@ def test_row_bookkeeping_on_shared_rows(inter, zero_padding):
 def test_default_workgroups():
     """Rows of at most two column chunks: one wave per row. Three chunks: at most one
     workgroup per CU, with no round of rows left mostly idle. Four or more: one workgroup
-    per row, its four waves sharing the row's chunks."""
+    per row, its four waves sharing the row's chunks. Never past the dispatch limit."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = WORKLOADS["headline"].rows
     # forward: pick_u's width; 2048 columns = 1 chunk, 6144 = 3 chunks, 8192 = 4 chunks
@@ -133,3 +133,9 @@ def test_default_workgroups():
         say(f"[launch] bwd inter {inter}: {wg} workgroups")
         assert wg == rows
     assert swiglu_probs_default_workgroups("bwd", rows, 1536) == -(-rows // 4)   # 3 vectors per lane
+    # a dispatch holds its work-item count in 32 bits: at most 16,777,215 workgroups of 256
+    for direction, r, inter in (("fwd", 67_108_860, 8), ("fwd", 70_000_000, 8), ("bwd", 70_000_000, 8),
+                                ("bwd", 16_777_216, 2048), ("fwd", 2_000_000_000, 8192)):
+        assert swiglu_probs_default_workgroups(direction, r, inter) == 16_777_215, (direction, r, inter)
+    assert swiglu_probs_default_workgroups("fwd", 67_108_859, 8) == 16_777_215
+    assert swiglu_probs_default_workgroups("fwd", 67_108_856, 8) == 16_777_214

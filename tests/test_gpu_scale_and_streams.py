@@ -54,6 +54,53 @@ def test_activation_past_4gib():
     say(f"[large] {sample.size} sampled rows ok")
 
 
+def test_row_counts_past_the_dispatch_limit():
+    """70 million rows of 8 columns. One wave per row would take 17.5 million workgroups,
+    past the 16,777,215 a dispatch can hold (its work-item count is 32 bits): the default
+    grid stops at that many, and the waves of the first 2.9 million rows take a second
+    row 67,108,860 rows on. Sampled rows on both sides of that seam, for the activation
+    and the soft-clamped squared ReLU, forward and backward, against the oracle."""
+    rows, inter = 70_000_000, 8
+    seam = 16_777_215 * 4
+    sample = np.unique(np.concatenate([np.arange(0, 4), np.arange(seam - 4, seam + 4),
+                                       np.arange(rows - 300, rows),
+                                       np.random.default_rng(5).integers(0, rows, 300)]))
+    idx = torch.from_numpy(sample).to(DEV)
+    g = torch.Generator(device=DEV).manual_seed(321)
+    say(f"[dispatch limit] activation rows={rows} inter={inter}")
+    x = (torch.randn(rows, 2 * inter, device=DEV, generator=g) * 3).to(torch.bfloat16)
+    probs = torch.rand(rows, device=DEV, generator=g)
+    gy = torch.randn(rows, inter, device=DEV, generator=g).to(torch.bfloat16)
+    y = torch.empty(rows, inter, dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty_like(x)
+    gp = torch.empty_like(probs)
+    swiglu_probs_fwd(x, probs, y, 7.0)
+    swiglu_probs_bwd(x, probs, gy, gx, gp, 7.0)
+    torch.cuda.synchronize()
+    xs, gys, ps = _bits(x[idx]), _bits(gy[idx]), probs[idx].cpu().numpy()
+    orc = oracle.get()
+    assert ulp_distance(_bits(y[idx]), orc.fwd(xs, ps, 7.0)).max() <= 1
+    want = orc.bwd(xs, ps, gys, 7.0)
+    assert ulp_distance(_bits(gx[idx]), want["grad_x"]).max() <= 1
+    assert grad_probs_violations(gp[idx].cpu().numpy(), want["grad_probs_f64"], want["row_scale"]).size == 0
+    del x, gx, y
+
+    say(f"[dispatch limit] squared ReLU rows={rows} hidden={inter}")
+    xq = (torch.randn(rows, inter, device=DEV, generator=g) * 6).to(torch.bfloat16)
+    yq = torch.empty_like(xq)
+    gxq = torch.empty_like(xq)
+    moe_squared_relu_probs_fwd(xq, probs, yq, clamp_scale=4.0)
+    moe_squared_relu_probs_bwd(xq, probs, gy, gxq, gp, clamp_scale=4.0)
+    torch.cuda.synchronize()
+    mo = moe_oracle.get()
+    xqs = _bits(xq[idx])
+    assert ulp_distance(_bits(yq[idx]), mo.squared_relu_probs(xqs, ps, clamp_scale=4.0)).max() <= 1
+    wq = mo.squared_relu_probs_bwd(xqs, ps, gys, clamp_scale=4.0)
+    assert ulp_distance(_bits(gxq[idx]), wq["grad_x"]).max() <= 1
+    assert grad_probs_violations(gp[idx].cpu().numpy(), wq["grad_probs_f64"], wq["row_scale"]).size == 0
+    say(f"[dispatch limit] {sample.size} sampled rows ok")
+
+
 def test_moe_ops_graph_replay():
     """One graph holding the squared ReLU forward and backward (device n_used) and the
     unpermute (device valid_tokens); both counts change between replays, with eager work

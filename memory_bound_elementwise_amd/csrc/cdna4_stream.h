@@ -57,9 +57,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 // length (0 for a row that is not live). Offsets are range-checked relative to the
 // resource, so every access uses only the lane's VGPR offset: lanes past the end
 // read zeros without touching memory and their stores are dropped.
+// Row lengths and offsets stay below 2^31 (the hosts bound row widths), so the
+// remaining length is taken as a signed max, which the scalar unit has. The unsigned
+// form (a saturating subtract) has only a vector instruction: each descriptor then
+// borrowed a VGPR, often one a pending load was about to fill, and the compiler
+// drained the loads in flight before the write.
 __device__ __forceinline__ rsrc_t chunk_rsrc(const void *row, uint32_t bytes, uint32_t off)
 {
-    return make_rsrc(reinterpret_cast<const char *>(row) + off, bytes > off ? bytes - off : 0u);
+    const int rem = (int)bytes - (int)off;
+    return make_rsrc(reinterpret_cast<const char *>(row) + off, (uint32_t)(rem > 0 ? rem : 0));
 }
 
 __device__ __forceinline__ u32x4 load_vec(rsrc_t r, uint32_t voff)

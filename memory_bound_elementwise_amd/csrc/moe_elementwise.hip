@@ -702,45 +702,52 @@ __global__ __launch_bounds__(kBlock) void unpermute_pipelined_kernel(const uint1
         }
     };
 
-    // current unit (t, c), token t being entry j of the map group held in mvs
+    // current unit (t, c), token t being entry j of its map group
     int64_t t = wave_id();
     if (t >= bound)
         return;
+    // map group of the next unit to issue. Only issue() reads it, and the current
+    // unit's gathers are already out, so a new group replaces it in place: one
+    // register, never copied (a copy through a register that a pending gather fills
+    // makes the compiler drain that gather first).
     int mvs = load_maps(t);
     int j = 0, c = 0;
-    // the next unit's chunk and map slot; a new map group is loaded when the next
-    // token starts one (its gathers need it at once)
-    int c1, j1, mvs1;
-    auto step = [&]() {
-        if (c + 1 < nch) {
-            c1 = c + 1, j1 = j, mvs1 = mvs;
-        } else if (j + 1 < kTokensPerMap) {
-            c1 = 0, j1 = j + 1, mvs1 = mvs;
-        } else {
-            c1 = 0, j1 = 0, mvs1 = load_maps(t + W);
-        }
+    // the unit after (c, j): the next chunk, else the next token of the map group,
+    // else the first token of a new group (whose map the gathers need at once)
+    struct Next {
+        int c, j;
+        bool group;
     };
-    auto advance = [&]() {
-        t = c1 == 0 ? t + W : t;
-        c = c1, j = j1, mvs = mvs1;
+    auto next = [nch](int c0, int j0) -> Next {
+        if (c0 + 1 < nch)
+            return {c0 + 1, j0, false};
+        if (j0 + 1 < kTokensPerMap)
+            return {0, j0 + 1, false};
+        return {0, 0, true};
     };
     // The scheduling barriers keep each unit's gathers ahead of the previous unit's
     // adds: the two are independent, and the scheduler would otherwise sink the loads.
     UnpermuteBuf<U, G> A, B;
     issue(A, 0, mvs, 0);
     for (;;) {
-        step();
-        issue(B, c1, mvs1, j1);
+        Next n = next(c, j);
+        if (n.group)
+            mvs = load_maps(t + W);
+        issue(B, n.c, mvs, n.j);
         __builtin_amdgcn_sched_barrier(0);
         finish(A, t, c);
-        advance();
+        t = n.c == 0 ? t + W : t;
+        c = n.c, j = n.j;
         if (t >= bound)
             break;
-        step();
-        issue(A, c1, mvs1, j1);
+        n = next(c, j);
+        if (n.group)
+            mvs = load_maps(t + W);
+        issue(A, n.c, mvs, n.j);
         __builtin_amdgcn_sched_barrier(0);
         finish(B, t, c);
-        advance();
+        t = n.c == 0 ? t + W : t;
+        c = n.c, j = n.j;
         if (t >= bound)
             break;
     }

@@ -85,6 +85,14 @@ def _dt(t: torch.Tensor, dtype: Optional[str]) -> int:
     return _TORCH[t.dtype]
 
 
+def _bf16_bits(name, *ts):
+    """bf16 tensors, or int16 / uint16 views of bf16 bit patterns (never fp16: its bits
+    would be read as bf16)."""
+    for t in ts:
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError(f"{name} must be bf16 (or its int16/uint16 bits), got {t.dtype}")
+
+
 def _dev(*ts):
     dev = None
     for t in ts:
@@ -166,7 +174,8 @@ def moe_router_weight_bwd(grad_out, x, probs, grad_x, grad_probs, *, out_dtype=N
 def moe_squared_relu_probs_fwd(x, probs, y, *, clamp_scale=None, n_used=None, permutation_map=None,
                                zero_padding=False, stream=None, num_workgroups=0):
     """Squared ReLU x probs (bf16 in and out); ``clamp_scale`` enables the tanh soft clamp."""
-    if x.dim() != 2 or y.shape != x.shape or x.element_size() != 2 or y.element_size() != 2:
+    _bf16_bits("x and y", x, y)
+    if x.dim() != 2 or y.shape != x.shape:
         raise ValueError("x and y must be bf16 [rows, hidden]")
     rows, hidden = x.shape
     if probs.dtype != torch.float32 or probs.numel() != rows:
@@ -192,8 +201,8 @@ def moe_squared_relu_probs_bwd(x, probs, grad_y, grad_x, grad_probs=None, *, cla
                                num_workgroups=0):
     """Backward of ``moe_squared_relu_probs_fwd``: grad_x (bf16) and, when given, grad_probs
     (fp32 [rows], indexed by slot; slots of rows that are not live are left as they are)."""
-    if x.dim() != 2 or x.element_size() != 2 or grad_y.shape != x.shape or grad_x.shape != x.shape \
-            or grad_y.element_size() != 2 or grad_x.element_size() != 2:
+    _bf16_bits("x, grad_y and grad_x", x, grad_y, grad_x)
+    if x.dim() != 2 or grad_y.shape != x.shape or grad_x.shape != x.shape:
         raise ValueError("x, grad_y and grad_x must be bf16 [rows, hidden]")
     rows, hidden = x.shape
     if probs.dtype != torch.float32 or probs.numel() != rows:
@@ -219,7 +228,8 @@ def moe_squared_relu_probs_bwd(x, probs, grad_y, grad_x, grad_probs=None, *, cla
 def moe_unpermute_expert_order(expert_output, inverse_map, out, *, valid_tokens=None,
                                out_dtype=None, stream=None, num_workgroups=0):
     """out[t] = sum over local experts e in increasing order of expert_output[inverse_map[t, e]]."""
-    if expert_output.dim() != 2 or expert_output.element_size() != 2:
+    _bf16_bits("expert_output", expert_output)
+    if expert_output.dim() != 2:
         raise ValueError("expert_output must be bf16 [rows, hidden]")
     if inverse_map.dim() != 2 or inverse_map.dtype != torch.int32:
         raise ValueError("inverse_map must be int32 [tokens, num_local_experts]")

@@ -2,9 +2,10 @@
 
 ``libswiglu_probs.so`` holds the activation kernels and their C ABI
 (``include/swiglu_probs.h``); ``libmoe_elementwise.so`` the MoE elementwise
-operations next to it (``include/moe_elementwise.h``); ``libhbm_probe.so`` holds plain streaming kernels
-that measure the practical HBM ceiling and calibrate the hardware byte counters
-(``include/hbm_probe.h``). Both are written to ``memory_bound_elementwise_amd/_lib``.
+operations next to it (``include/moe_elementwise.h``); ``libhbm_probe.so`` plain
+streaming kernels that measure the practical HBM ceiling and calibrate the hardware
+byte counters (``include/hbm_probe.h``). All three are written to
+``memory_bound_elementwise_amd/_lib``.
 """
 from __future__ import annotations
 

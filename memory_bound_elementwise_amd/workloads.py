@@ -1,6 +1,8 @@
-"""Seeded synthetic inputs for the clamped SwiGLU x probs activation.
+"""Seeded synthetic inputs for the clamped SwiGLU x probs activation and for the MoE
+elementwise operations beside it (``make_moe_inputs``), with their algorithmic byte
+counts.
 
-This module draws inputs only; it holds none of the activation's arithmetic and
+This module draws inputs only; it holds none of the operations' arithmetic and
 serves both the HIP path and the CPU oracle (through the tests and the bench).
 Every array is drawn on the CPU from ``torch.Generator().manual_seed(seed)`` in
 a fixed order, so both sides see the same bytes:

@@ -20,10 +20,11 @@ numpy arrays. Sources, per function:
   finite-difference and brute-force pins.
 * ``bf16_rne``: fp32 -> bf16, round to nearest even (the single final rounding).
 
-Pinning: every function here is checked in ``tests/test_oracle_pins.py`` against
+Pinning: every function here is checked by ``tests/test_oracle_pins.py`` against
 values fixed independently of it (torch library routines, fp64 autograd, central
-finite differences, closed forms, brute force, structural invariants); see the
-module docstring of that file for which pin covers which part.
+finite differences, closed forms, brute force, structural invariants). The pins
+live in ``tests/oracle_pins.py``, whose module docstring maps each part of the
+oracle to the pin that checks it.
 """
 from __future__ import annotations
 

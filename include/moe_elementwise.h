@@ -47,8 +47,9 @@ typedef enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype_t;
 
 typedef enum moe_status {
     MOE_OK = 0,
-    MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, dtype, scale or
-                                 workgroup count, overlap */
+    MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size (negative; rows or
+                                 tokens above 2,143,289,343; hidden above 2^26), dtype,
+                                 scale or workgroup count, overlap */
     MOE_ERR_ALIGNMENT = 2,    /* misaligned pointer, or a row width not a multiple of 8 */
     MOE_ERR_HIP = 3           /* launch failed; see moe_elementwise_last_hip_error */
 } moe_status_t;

@@ -62,9 +62,9 @@ extern "C" {
 
 typedef enum swiglu_status {
     SWIGLU_OK = 0,
-    /* a required pointer is NULL, rows < 0, inter <= 0, rows or inter too large,
-     * limit is NaN or <= 0, num_workgroups < 0 or > 16,777,215, or an output
-     * overlaps an input */
+    /* a required pointer is NULL, rows < 0, inter <= 0, rows > 2,143,289,343,
+     * inter > 2^28 (268,435,456), limit is NaN or <= 0, num_workgroups < 0 or
+     * > 16,777,215, or an output overlaps an input */
     SWIGLU_ERR_INVALID_ARG = 1,
     /* inter % 8 != 0, or a base pointer misses its alignment (16 B for bf16
      * tensors, 4 B for fp32/int32) */

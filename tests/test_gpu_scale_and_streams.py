@@ -54,6 +54,42 @@ def test_activation_past_4gib():
     say(f"[large] {sample.size} sampled rows ok")
 
 
+def test_widest_rows():
+    """inter = 2^28, the widest row the C ABI accepts: each row is 131,072 column chunks
+    of four vectors per lane, shared by a workgroup's four waves, with chunk offsets up
+    to 2^29 bytes. Two rows, every element against the oracle (compared in slices)."""
+    rows, inter = 2, 1 << 28
+    g = torch.Generator(device=DEV).manual_seed(11)
+    say(f"[widest] rows={rows} inter={inter}")
+    x = (torch.randn(rows, 2 * inter, device=DEV, generator=g) * 3).to(torch.bfloat16)
+    probs = torch.rand(rows, device=DEV, generator=g)
+    gy = torch.randn(rows, inter, device=DEV, generator=g).to(torch.bfloat16)
+    y = torch.empty(rows, inter, dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty_like(x)
+    gp = torch.empty_like(probs)
+    swiglu_probs_fwd(x, probs, y, 7.0)
+    swiglu_probs_bwd(x, probs, gy, gx, gp, 7.0)
+    torch.cuda.synchronize()
+    xs, gys, ps = _bits(x), _bits(gy), probs.cpu().numpy()
+    del x, gy
+    say("[widest] kernels done; oracle forward")
+    orc = oracle.get()
+    want_y = orc.fwd(xs, ps, 7.0)
+    got = _bits(y).reshape(-1)
+    step = 1 << 24
+    for i in range(0, got.size, step):
+        assert ulp_distance(got[i:i + step], want_y.reshape(-1)[i:i + step]).max() <= 1, f"y at {i}"
+    del want_y, got, y
+    say("[widest] y ok; oracle backward")
+    want = orc.bwd(xs, ps, gys, 7.0)
+    got = _bits(gx).reshape(-1)
+    wgx = want["grad_x"].reshape(-1)
+    for i in range(0, got.size, step):
+        assert ulp_distance(got[i:i + step], wgx[i:i + step]).max() <= 1, f"grad_x at {i}"
+    assert grad_probs_violations(gp.cpu().numpy(), want["grad_probs_f64"], want["row_scale"]).size == 0
+    say("[widest] ok")
+
+
 def test_row_counts_past_the_dispatch_limit():
     """70 million rows of 8 columns. One wave per row would take 17.5 million workgroups,
     past the 16,777,215 a dispatch can hold (its work-item count is 32 bits): the default

@@ -509,3 +509,55 @@ def test_moe_error_paths():
     a = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
     assert lib.moe_residual_add(a.data_ptr() + 2, a.data_ptr(), a.data_ptr(), a.data_ptr(), 8, 0, None, 0) == 2
     say("[moe] error paths ok")
+
+
+def test_widest_rows():
+    """hidden = 2^26, the widest row the MoE C ABI accepts (an fp32 row is 2^28 bytes):
+    router weight forward and backward in fp32, the soft-clamped squared ReLU forward and
+    backward, and the unpermute with fp32 output, on two rows or tokens each; every
+    element against the oracle."""
+    H = 1 << 26
+    rng = np.random.default_rng(26)
+    orc = moe_oracle.get()
+    say(f"[moe widest] router fp32, 2 x {H}")
+    x = _rand((2, H), "f32", rng, 3.0, specials=False)
+    g = _rand((2, H), "f32", rng, 1.0, specials=False)
+    p = rng.uniform(0, 1, 2).astype(np.float32)
+    dp = torch.from_numpy(p).to(DEV)
+    xd, gd = _dev(x, "f32"), _dev(g, "f32")
+    out = torch.empty((2, H), dtype=torch.float32, device=DEV)
+    gx = torch.empty_like(out)
+    gp = torch.full((2,), -7.0, device=DEV)
+    moe_router_weight_fwd(xd, dp, out)
+    moe_router_weight_bwd(gd, xd, dp, gx, gp)
+    torch.cuda.synchronize()
+    assert _same(_host(out, "f32"), orc.router_weight_fwd(x, "f32", p, "f32"), "f32"), "router fwd"
+    ref = orc.router_weight_bwd(g, "f32", x, "f32", p)
+    assert _same(_host(gx, "f32"), ref["grad_x"], "f32"), "router grad_x"
+    assert grad_probs_violations(gp.cpu().numpy(), ref["grad_probs_f64"], ref["row_scale"]).size == 0
+    del x, g, xd, gd, out, gx, ref
+
+    say(f"[moe widest] squared ReLU, 2 x {H}")
+    xb = _rand((2, H), "bf16", rng, 6.0, specials=False)
+    gb = _rand((2, H), "bf16", rng, 1.0, specials=False)
+    xbd = _dev(xb, "bf16")
+    yq = torch.empty_like(xbd)
+    moe_squared_relu_probs_fwd(xbd, dp, yq, clamp_scale=4.0)
+    torch.cuda.synchronize()
+    assert_within_ulp(_host(yq, "bf16"), orc.squared_relu_probs(xb, p, clamp_scale=4.0), 1, "sqrelu fwd")
+    gxq = torch.empty_like(xbd)
+    gpq = torch.full((2,), GP_SENTINEL, device=DEV)
+    moe_squared_relu_probs_bwd(xbd, dp, _dev(gb, "bf16"), gxq, gpq, clamp_scale=4.0)
+    torch.cuda.synchronize()
+    _check_sqb(_host(gxq, "bf16"), gpq.cpu().numpy(),
+               orc.squared_relu_probs_bwd(xb, p, gb, clamp_scale=4.0), 4.0, "sqrelu widest")
+    del xb, gb, xbd, yq, gxq
+
+    say(f"[moe widest] unpermute fp32, 2 tokens x 2 experts x {H}")
+    eo = _rand((3, H), "bf16", rng, 1.0, specials=False)
+    im = np.array([[0, 1], [2, -1]], np.int32)
+    uo = torch.empty((2, H), dtype=torch.float32, device=DEV)
+    moe_unpermute_expert_order(_dev(eo, "bf16"), torch.from_numpy(im).to(DEV), uo)
+    torch.cuda.synchronize()
+    assert _same(_host(uo, "f32"), orc.unpermute(eo, im, "f32"), "f32"), "unpermute"
+    say("[moe widest] ok")

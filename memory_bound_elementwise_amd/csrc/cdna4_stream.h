@@ -207,43 +207,59 @@ __device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, cons
         const int nk = left < kWave ? (int)left : kWave;
         const int T = nk * nch;
 
-        auto item = [&](int t, int &k, int &c) {
-            k = (nch == 1) ? t : t / nch;
-            c = t - k * nch;
-            if (k >= nk) k = nk - 1;  // past the end: any row of the batch, empty resource
+        // Item t is (row k of the batch, chunk c), t = k * nch + c. The loads and the
+        // processing each keep a cursor and step it, rather than dividing t. The rows of
+        // a batch lie below 2^31 (the hosts bound the row count), so their indices are
+        // 32-bit: 64-bit compares and divisions have no scalar form, and the vector
+        // registers they borrow can be ones a pending load is about to fill, which the
+        // compiler then waits on.
+        auto step = [nch](int &k, int &c) {
+            if (++c == nch) {
+                c = 0;
+                ++k;
+            }
         };
         // Without a map a row is live iff it is below the live bound, so its loads do
-        // not wait for the metadata gather; with a map the slot decides.
-        auto prefetch = [&](int t, typename Op::Buf &buf) {
-            int k, c;
-            item(t, k, c);
-            const int64_t r = base + (int64_t)k * W;
+        // not wait for the metadata gather; with a map the slot decides. Past the last
+        // item the load names the batch's last row through an empty resource.
+        auto prefetch = [&](int t, int k, int c, typename Op::Buf &buf) {
+            if (k >= nk)
+                k = nk - 1;
+            const int r = (int)base + k * W;
             const bool live = perm ? __builtin_amdgcn_readlane(slot_l, k) >= 0 : r < sched.live;
             op.load(buf, r, c, live && t < T);
         };
-        auto process = [&](int t, const typename Op::Buf &buf) {
-            int k, c;
-            item(t, k, c);
+        auto process = [&](int k, int c, const typename Op::Buf &buf) {
             const int slot = __builtin_amdgcn_readlane(slot_l, k);
             const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
             if (c == 0)
                 row_sum_reset(op);
-            op.process(buf, base + (int64_t)k * W, c, slot, p);
+            op.process(buf, (int)base + k * W, c, slot, p);
             if constexpr (Op::kRowSum) {
                 if (c == nch - 1 && slot >= 0 && op.row_sum_wanted())
                     op.store_row_sum(slot, wave_sum(op.acc));
             }
         };
 
+        // The scheduling barriers keep each item's loads ahead of the previous item's
+        // arithmetic, which the scheduler would otherwise hoist above them.
         typename Op::Buf A, B;
-        prefetch(0, A);
+        int pk = 0, pc = 0, qk = 0, qc = 0;  // next item to load, next item to process
+        prefetch(0, pk, pc, A);
+        step(pk, pc);
         for (int t = 0; t < T; t += 2) {
-            prefetch(t + 1, B);
-            process(t, A);
+            prefetch(t + 1, pk, pc, B);
+            step(pk, pc);
+            __builtin_amdgcn_sched_barrier(0);
+            process(qk, qc, A);
+            step(qk, qc);
             if (t + 1 >= T)
                 break;
-            prefetch(t + 2, A);
-            process(t + 1, B);
+            prefetch(t + 2, pk, pc, A);
+            step(pk, pc);
+            __builtin_amdgcn_sched_barrier(0);
+            process(qk, qc, B);
+            step(qk, qc);
         }
     }
 }
@@ -283,29 +299,29 @@ __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched,
         const int nk = left < kWave ? (int)left : kWave;
         const int T = nk * nc;
 
-        auto item = [&](int t, int &k, int &j) {
-            k = (nc == 1) ? t : t / nc;
-            j = t - k * nc;
-            if (k >= nk) k = nk - 1;
+        // items (row k, the wave's chunk j), stepped as in walk_rows
+        auto step = [nc](int &k, int &jj) {
+            if (++jj == nc) {
+                jj = 0;
+                ++k;
+            }
         };
-        auto prefetch = [&](int t, typename Op::Buf &buf) {
-            int k, j;
-            item(t, k, j);
-            const int64_t r = base + (int64_t)k * G;
+        auto prefetch = [&](int t, int k, int jj, typename Op::Buf &buf) {
+            if (k >= nk)
+                k = nk - 1;
+            const int r = (int)base + k * G;
             const bool live = perm ? __builtin_amdgcn_readlane(slot_l, k) >= 0 : r < sched.live;
-            op.load(buf, r, c_lo + j, live && t < T);
+            op.load(buf, r, c_lo + jj, live && t < T);
         };
-        auto process = [&](int t, const typename Op::Buf &buf) {
-            int k, j;
-            item(t, k, j);
+        auto process = [&](int k, int jj, const typename Op::Buf &buf) {
             const int slot = __builtin_amdgcn_readlane(slot_l, k);
             const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p_l), k));
-            if (j == 0)
+            if (jj == 0)
                 row_sum_reset(op);
-            op.process(buf, base + (int64_t)k * G, c_lo + j, slot, p);
+            op.process(buf, (int)base + k * G, c_lo + jj, slot, p);
             if constexpr (Op::kRowSum) {
                 // slot and the op's state are the same for all four waves: all or none sync
-                if (j == nc - 1 && slot >= 0 && op.row_sum_wanted()) {
+                if (jj == nc - 1 && slot >= 0 && op.row_sum_wanted()) {
                     const float part = wave_sum(op.acc);
                     if (lane == 0)
                         partials[parity][w] = part;
@@ -323,14 +339,22 @@ __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched,
         };
 
         typename Op::Buf A, B;
-        prefetch(0, A);
+        int pk = 0, pj = 0, qk = 0, qj = 0;  // next item to load, next item to process
+        prefetch(0, pk, pj, A);
+        step(pk, pj);
         for (int t = 0; t < T; t += 2) {
-            prefetch(t + 1, B);
-            process(t, A);
+            prefetch(t + 1, pk, pj, B);
+            step(pk, pj);
+            __builtin_amdgcn_sched_barrier(0);
+            process(qk, qj, A);
+            step(qk, qj);
             if (t + 1 >= T)
                 break;
-            prefetch(t + 2, A);
-            process(t + 1, B);
+            prefetch(t + 2, pk, pj, A);
+            step(pk, pj);
+            __builtin_amdgcn_sched_barrier(0);
+            process(qk, qj, B);
+            step(qk, qj);
         }
     }
 }

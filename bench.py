@@ -262,7 +262,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first; the first ~30 steps of sustained work run through a "
+                         "start-up clock transient on MI355X")
     ap.add_argument("--workload", default="headline",
                     choices=["tiny", "mid", "headline", "padded", "edge"])
     ap.add_argument("--op", default="swiglu_probs", choices=["swiglu_probs"] + sorted(MOE_OPS),

@@ -325,7 +325,12 @@ __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched,
                     const float part = wave_sum(op.acc);
                     if (lane == 0)
                         partials[parity][w] = part;
-                    __syncthreads();
+                    // A barrier fenced on LDS alone: only the partials cross it, and
+                    // __syncthreads would also wait for every global access in flight,
+                    // the next item's prefetched loads included.
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
                     if (w == 0) {
                         float total = partials[parity][0];
 #pragma unroll

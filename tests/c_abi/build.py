@@ -1,8 +1,8 @@
-"""Build the plain-C check of the activation's C ABI (test infrastructure).
+"""Build the plain-C checks of the C ABIs (test infrastructure).
 
-The program links the HIP library (memory_bound_elementwise_amd/_lib) and the CPU
-oracle (oracle/liboracle_swiglu.so) and finds them at run time through rpaths
-relative to its own location, so the built tree can move.
+swiglu_c_check links the activation's HIP library and its CPU oracle; moe_c_check
+links the MoE elementwise library and the MoE oracle. Both find the libraries at run
+time through rpaths relative to their own location, so the built tree can move.
 """
 from __future__ import annotations
 
@@ -12,30 +12,40 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
-SOURCE = os.path.join(HERE, "swiglu_c_check.c")
-BINARY = os.path.join(HERE, "swiglu_c_check")
+
+# program -> (HIP library, oracle library)
+PROGRAMS = {
+    "swiglu_c_check": ("swiglu_probs", "oracle_swiglu"),
+    "moe_c_check": ("moe_elementwise", "oracle_moe"),
+}
 
 
-def build() -> str:
+def _build_one(name: str, hip_lib: str, oracle_lib: str) -> str:
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         raise RuntimeError("no C compiler for the C ABI check")
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     lib = os.path.join(ROOT, "memory_bound_elementwise_amd", "_lib")
     orc = os.path.join(ROOT, "oracle")
-    tmp = BINARY + ".tmp"
+    binary = os.path.join(HERE, name)
+    tmp = binary + ".tmp"
     cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
-           f"-I{ROOT}/include", "-isystem", f"{rocm}/include", SOURCE, "-o", tmp,
-           f"-L{lib}", "-lswiglu_probs", f"-L{orc}", "-loracle_swiglu", f"-L{rocm}/lib", "-lamdhip64",
+           f"-I{ROOT}/include", "-isystem", f"{rocm}/include", os.path.join(HERE, name + ".c"), "-o", tmp,
+           f"-L{lib}", f"-l{hip_lib}", f"-L{orc}", f"-l{oracle_lib}", f"-L{rocm}/lib", "-lamdhip64",
            "-lm", "-lpthread",
            "-Wl,-rpath,$ORIGIN/../../memory_bound_elementwise_amd/_lib",
            "-Wl,-rpath,$ORIGIN/../../oracle", f"-Wl,-rpath,{rocm}/lib"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"build of the C ABI check failed:\n{' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, BINARY)
-    return BINARY
+        raise RuntimeError(f"build of {name} failed:\n{' '.join(cmd)}\n{res.stderr}")
+    os.replace(tmp, binary)
+    return binary
+
+
+def build() -> list[str]:
+    return [_build_one(name, *libs) for name, libs in PROGRAMS.items()]
 
 
 if __name__ == "__main__":
-    print(build())
+    for path in build():
+        print(path)

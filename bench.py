@@ -96,6 +96,56 @@ MOE_OPS = {
 }
 
 
+class TimingEvents:
+    """HIP events for timing only, on torch's current stream of cuda:0 (the stream the
+    kernels are launched on). They are created with hipEventDisableSystemFence: recording
+    a default event also makes a system-scope release, whose cache writeback the stream
+    waits for, and timing needs only the timestamps (the final device synchronisation
+    orders everything). On MI355X that took a fwd+bwd step with two events from 281.6 to
+    278.0 us (275.0 with none). torch's Event cannot be given the flag, so this calls
+    the HIP runtime torch has loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count: int):
+        import ctypes
+        import torch
+        self._ct = ctypes
+        self._hip = hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._stream = ctypes.c_void_p(torch.cuda.current_stream(0).cuda_stream)
+        self._ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            rc = hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                self.close()
+                raise RuntimeError(f"hipEventCreateWithFlags failed: hipError_t {rc}")
+            self._ev.append(e)
+
+    def record(self, i: int) -> None:
+        rc = self._hip.hipEventRecord(self._ev[i], self._stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: hipError_t {rc}")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        """Milliseconds from event i to event j; both must have completed."""
+        ms = self._ct.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ct.byref(ms), self._ev[i], self._ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: hipError_t {rc}")
+        return float(ms.value)
+
+    def close(self) -> None:
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
+
+
 def time_kernels(kernels, steps, warmup, cold_reps):
     """kernels: list of (name, launch), one step being each launched once in order.
     Returns wall ms per step, per-kernel event times (lists, ms) over the timed steps,
@@ -103,10 +153,10 @@ def time_kernels(kernels, steps, warmup, cold_reps):
 
     One event is recorded before the first launch and one after every launch, on the
     launch stream, so each launch lies between two events and consecutive launches
-    share the one between them. Each recorded event costs the stream a few
-    microseconds (measured on MI355X: 2 events per fwd+bwd step instead of 3 took the
-    step from 283 to 278 us; with none it is 272 us), so no more are recorded than
-    the per-launch durations need."""
+    share the one between them. Each recorded event costs the stream time (on MI355X,
+    with torch's default events, 2 per fwd+bwd step instead of 3 took the step from 283
+    to 278 us; with none it was 272 us), so no more are recorded than the per-launch
+    durations need, and they are TimingEvents, which skip the system-scope fence."""
     import numpy as np
     import torch
     for _ in range(warmup):
@@ -114,30 +164,32 @@ def time_kernels(kernels, steps, warmup, cold_reps):
             fn()
     torch.cuda.synchronize()
     n = len(kernels)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * n + 1)]
+    ev = TimingEvents(steps * n + 1)
     t0 = time.perf_counter()
-    ev[0].record()
+    ev.record(0)
     for s in range(steps):
         for i, (_, fn) in enumerate(kernels):
             fn()
-            ev[s * n + i + 1].record()
+            ev.record(s * n + i + 1)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = {name: [ev[s * n + i].elapsed_time(ev[s * n + i + 1]) for s in range(steps)]
+    per = {name: [ev.elapsed_ms(s * n + i, s * n + i + 1) for s in range(steps)]
            for i, (name, _) in enumerate(kernels)}
+    ev.close()
     cold = {}
     if cold_reps > 0:
         evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
         for name, fn in kernels:
             ts = []
+            ev = TimingEvents(2)
             for _ in range(cold_reps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 evict.sum(dtype=torch.int64)
-                a.record()
+                ev.record(0)
                 fn()
-                b.record()
+                ev.record(1)
                 torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b))
+                ts.append(ev.elapsed_ms(0, 1))
+            ev.close()
             cold[name] = float(np.median(ts))
         del evict
     return wall, per, cold
@@ -352,14 +404,15 @@ def main() -> int:
             srcs, dsts = bufs[:ns], bufs[3:3 + nd]
             for _ in range(3):
                 hbm_probe_stream(srcs, dsts)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev = TimingEvents(2)
             reps = 20
-            ev[0].record()
+            ev.record(0)
             for _ in range(reps):
                 hbm_probe_stream(srcs, dsts)
-            ev[1].record()
+            ev.record(1)
             torch.cuda.synchronize()
-            ms = ev[0].elapsed_time(ev[1]) / reps
+            ms = ev.elapsed_ms(0, 1) / reps
+            ev.close()
             moved = (ns + nd) * nvec_elems * 2
             probe[name] = {"bytes": moved, "us": round(ms * 1e3, 2),
                            "GB/s": round(moved / (ms * 1e6), 1),

@@ -266,7 +266,9 @@ __device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, cons
 
 // A workgroup's walk over its rows (row r, r + G, r + 2G, ... for workgroup r of G), the
 // four waves sharing each row: wave w takes the column chunks
-// [floor(w nch / 4), floor((w + 1) nch / 4)), at least one each for nch >= 4. Per wave the
+// [floor(w nch / 4), floor((w + 1) nch / 4)), at least one each for nch >= 4. With
+// `spans` (uniform), the op has already given each wave its own quarter of the row and
+// nch counts the chunks of one quarter: every wave takes all nch of them. Per wave the
 // items (row, chunk) run through the same two-buffer pipeline as walk_rows. Row sums
 // (kRowSum ops) combine each wave's partial with wave_sum, then the four partials in
 // wave order through LDS, one barrier per row; the LDS pair alternates by row so a
@@ -274,9 +276,10 @@ __device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, cons
 // workgroup visits the same rows, so every barrier is reached by all four.
 template <class Op>
 __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched, const int *__restrict__ perm,
-                                               const float *__restrict__ probs, int nch)
+                                               const float *__restrict__ probs, int nch,
+                                               bool spans = false)
 {
-    if (nch < kWavesPerBlock) {
+    if (!spans && nch < kWavesPerBlock) {
         // a wave without chunks would miss the barriers: rows this short go one per wave
         // (the condition is the same for the whole grid)
         walk_rows(op, sched, perm, probs, nch);
@@ -286,8 +289,8 @@ __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched,
     const int lane = lane_id();
     const int G = gridDim.x;
     const int w = wave_in_block();
-    const int c_lo = (int)((int64_t)w * nch / kWavesPerBlock);
-    const int nc = (int)((int64_t)(w + 1) * nch / kWavesPerBlock) - c_lo;  // >= 1 for nch >= 4
+    const int c_lo = spans ? 0 : (int)((int64_t)w * nch / kWavesPerBlock);
+    const int nc = spans ? nch : (int)((int64_t)(w + 1) * nch / kWavesPerBlock) - c_lo;  // >= 1
     const int wg = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
     int parity = 0;
 

@@ -216,6 +216,8 @@ __global__ __launch_bounds__(kBlock) void residual_add_kernel(const char *e, con
 // ---------------------------------------------------------------------------
 // Router-weight multiply
 // ---------------------------------------------------------------------------
+// A wave covers octs [oct0, oct0 + octs) of each row it visits: the whole row, or its
+// quarter of the row when the four waves of a workgroup split rows into equal spans.
 template <int XDT, int ODT, int U>
 struct RouterFwdOp {
     static constexpr bool kRowSum = false;
@@ -225,12 +227,14 @@ struct RouterFwdOp {
     const char *x;
     char *out;
     int hidden;
+    uint32_t oct0, octs;
     uint32_t lane;
 
     __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
     {
         const uint32_t row = (uint32_t)hidden * kElemBytes<XDT>;
-        const rsrc_t rx = chunk_rsrc(x + r * row, live ? row : 0u, (uint32_t)c * U * kWave * kOctBytes<XDT>);
+        const rsrc_t rx = chunk_rsrc(x + r * row + oct0 * kOctBytes<XDT>, live ? octs * kOctBytes<XDT> : 0u,
+                                     (uint32_t)c * U * kWave * kOctBytes<XDT>);
 #pragma unroll
         for (int u = 0; u < U; ++u)
             b.x[u] = load_oct<XDT>(rx, (lane + u * kWave) * kOctBytes<XDT>);
@@ -239,7 +243,7 @@ struct RouterFwdOp {
     __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p) const
     {
         const uint32_t row = (uint32_t)hidden * kElemBytes<ODT>;
-        const rsrc_t ro = chunk_rsrc(out + r * row, slot >= 0 ? row : 0u,
+        const rsrc_t ro = chunk_rsrc(out + r * row + oct0 * kOctBytes<ODT>, slot >= 0 ? octs * kOctBytes<ODT> : 0u,
                                      (uint32_t)c * U * kWave * kOctBytes<ODT>);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -253,14 +257,31 @@ struct RouterFwdOp {
     }
 };
 
+// The wave's span of each row: the whole row, or with `spans` the wave's quarter.
+struct RowSpan {
+    uint32_t oct0, octs;
+    int nch;  // chunks of U * 64 octs in the span
+};
+
+template <int U>
+__device__ __forceinline__ RowSpan row_span(int hidden, int spans)
+{
+    const uint32_t row_octs = (uint32_t)hidden / 8;
+    RowSpan sp;
+    sp.octs = spans ? row_octs / kWavesPerBlock : row_octs;
+    sp.oct0 = spans ? (uint32_t)wave_in_block() * sp.octs : 0u;
+    sp.nch = (int)((sp.octs + U * kWave - 1) / (U * kWave));
+    return sp;
+}
+
 template <int XDT, int ODT, int U>
 __global__ __launch_bounds__(kBlock) void router_weight_fwd_kernel(const char *x, const float *probs,
-                                                                   char *out, int tokens, int hidden)
+                                                                   char *out, int tokens, int hidden, int spans)
 {
     const RowSchedule sched = make_schedule(tokens, nullptr, 0);
-    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
-    RouterFwdOp<XDT, ODT, U> op{x, out, hidden, (uint32_t)lane_id()};
-    walk_row_split(op, sched, nullptr, probs, nch);
+    const RowSpan sp = row_span<U>(hidden, spans);
+    RouterFwdOp<XDT, ODT, U> op{x, out, hidden, sp.oct0, sp.octs, (uint32_t)lane_id()};
+    walk_row_split(op, sched, nullptr, probs, sp.nch, spans != 0);
 }
 
 template <int XDT, int ODT, int U>
@@ -274,15 +295,18 @@ struct RouterBwdOp {
     char *gx;
     float *gp;
     int hidden;
+    uint32_t oct0, octs;
     uint32_t lane;
     float acc;  // this lane's partial of the current row's probability gradient
 
     __device__ __forceinline__ void load(Buf &b, int64_t r, int c, bool live) const
     {
         const uint32_t grow = (uint32_t)hidden * kElemBytes<ODT>, xrow = (uint32_t)hidden * kElemBytes<XDT>;
-        const rsrc_t rg = chunk_rsrc(g + r * grow, live ? grow : 0u, (uint32_t)c * U * kWave * kOctBytes<ODT>);
+        const rsrc_t rg = chunk_rsrc(g + r * grow + oct0 * kOctBytes<ODT>, live ? octs * kOctBytes<ODT> : 0u,
+                                     (uint32_t)c * U * kWave * kOctBytes<ODT>);
         // x is read only for the probability gradient
-        const rsrc_t rx = chunk_rsrc(x + r * xrow, live && gp ? xrow : 0u, (uint32_t)c * U * kWave * kOctBytes<XDT>);
+        const rsrc_t rx = chunk_rsrc(x + r * xrow + oct0 * kOctBytes<XDT>, live && gp ? octs * kOctBytes<XDT> : 0u,
+                                     (uint32_t)c * U * kWave * kOctBytes<XDT>);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             b.g[u] = load_oct<ODT>(rg, (lane + u * kWave) * kOctBytes<ODT>);
@@ -293,7 +317,7 @@ struct RouterBwdOp {
     __device__ __forceinline__ void process(const Buf &b, int64_t r, int c, int slot, float p)
     {
         const uint32_t xrow = (uint32_t)hidden * kElemBytes<XDT>;
-        const rsrc_t rgx = chunk_rsrc(gx + r * xrow, slot >= 0 && gx ? xrow : 0u,
+        const rsrc_t rgx = chunk_rsrc(gx + r * xrow + oct0 * kOctBytes<XDT>, slot >= 0 && gx ? octs * kOctBytes<XDT> : 0u,
                                       (uint32_t)c * U * kWave * kOctBytes<XDT>);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -320,12 +344,12 @@ struct RouterBwdOp {
 template <int XDT, int ODT, int U>
 __global__ __launch_bounds__(kBlock) void router_weight_bwd_kernel(const char *g, const char *x,
                                                                    const float *probs, char *gx,
-                                                                   float *gp, int tokens, int hidden)
+                                                                   float *gp, int tokens, int hidden, int spans)
 {
     const RowSchedule sched = make_schedule(tokens, nullptr, 0);
-    const int nch = (hidden / 8 + U * kWave - 1) / (U * kWave);
-    RouterBwdOp<XDT, ODT, U> op{g, x, gx, gp, hidden, (uint32_t)lane_id(), 0.0f};
-    walk_row_split(op, sched, nullptr, probs, nch);
+    const RowSpan sp = row_span<U>(hidden, spans);
+    RouterBwdOp<XDT, ODT, U> op{g, x, gx, gp, hidden, sp.oct0, sp.octs, (uint32_t)lane_id(), 0.0f};
+    walk_row_split(op, sched, nullptr, probs, sp.nch, spans != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -827,6 +851,53 @@ int pick_u(int64_t octs)
 // Column chunks of a row of `octs` octs at U octs per lane.
 int64_t row_chunks(int64_t octs, int U) { return (octs + (int64_t)U * kWave - 1) / ((int64_t)U * kWave); }
 
+// How the router-weight kernels cover their rows.
+//   * Rows of 4 or more chunks are shared by a workgroup's four waves, which take
+//     consecutive runs of whole chunks (7168 columns: 7 chunks of 128 octs, taken 1, 2,
+//     2, 2).
+//   * The backward meets its four waves at a barrier at the end of every row (for the row
+//     sum), so there the wave with one chunk waits for the others. When the chunks do not
+//     divide evenly over four, each of its waves instead takes an equal quarter of the
+//     row (224 octs: one chunk of U = 4 whose last 32 lane slots the range check masks),
+//     provided its slowest wave covers no more lane slots than the chunk split's. The row
+//     sum still combines the four quarters in order. At 53760 x 7168 (bf16) that took
+//     the backward from 377 to 372 us; quarters of two U = 2 chunks, or U = 1, were no
+//     faster than the split. The forward, with no barrier, stays on the split (quarters
+//     measured 0.3-1% slower).
+//   * Shorter rows go one per wave (walk_row_split falls back to walk_rows).
+// MOE_ROUTER_SPANS = 0 turns the quarters off, 1 takes them in both directions whenever
+// the row splits into quarters of whole octs.
+#ifndef MOE_ROUTER_SPANS
+#define MOE_ROUTER_SPANS -1
+#endif
+
+struct RouterPlan {
+    int U;
+    int spans;
+    int blocks;
+};
+
+RouterPlan plan_router(int64_t tokens, int64_t hidden, int cus, int num_workgroups, bool backward)
+{
+    const int64_t octs = hidden / 8;
+    RouterPlan pl{pick_u(octs), 0, 0};
+    const int64_t nch = row_chunks(octs, pl.U);
+    if (octs % kWavesPerBlock == 0 && nch >= kWavesPerBlock &&
+        (MOE_ROUTER_SPANS == 1 || (MOE_ROUTER_SPANS != 0 && backward))) {
+        const int64_t q = octs / kWavesPerBlock;
+        const int Uq = pick_u(q);
+        const int64_t span_slots = row_chunks(q, Uq) * Uq;                      // per lane
+        const int64_t split_slots = (nch + kWavesPerBlock - 1) / kWavesPerBlock * pl.U;
+        if (MOE_ROUTER_SPANS == 1 || (nch % kWavesPerBlock != 0 && span_slots <= split_slots)) {
+            pl.U = Uq;
+            pl.spans = 1;
+        }
+    }
+    pl.blocks = num_workgroups > 0 ? num_workgroups
+                                   : split_walk_workgroups(tokens, pl.spans ? kWavesPerBlock : nch, cus, 1);
+    return pl;
+}
+
 moe_status_t launched()
 {
     const hipError_t e = hipGetLastError();
@@ -845,41 +916,42 @@ void launch_residual(int blocks, hipStream_t st, const void *e, const void *s, c
 
 // router weight dispatch -----------------------------------------------------
 template <int XDT, int ODT, int U>
-void launch_router_fwd_u(int blocks, hipStream_t st, const void *x, const float *p, void *o, int t, int h)
+void launch_router_fwd_u(int blocks, hipStream_t st, const void *x, const float *p, void *o, int t, int h,
+                         int spans)
 {
     hipLaunchKernelGGL((router_weight_fwd_kernel<XDT, ODT, U>), dim3(blocks), dim3(kBlock), 0, st,
-                       static_cast<const char *>(x), p, static_cast<char *>(o), t, h);
+                       static_cast<const char *>(x), p, static_cast<char *>(o), t, h, spans);
 }
 
 template <int XDT, int ODT>
-void launch_router_fwd(int U, int blocks, hipStream_t st, const void *x, const float *p, void *o, int t, int h)
+void launch_router_fwd(const RouterPlan &pl, hipStream_t st, const void *x, const float *p, void *o, int t, int h)
 {
-    switch (U) {
-    case 1: launch_router_fwd_u<XDT, ODT, 1>(blocks, st, x, p, o, t, h); break;
-    case 2: launch_router_fwd_u<XDT, ODT, 2>(blocks, st, x, p, o, t, h); break;
-    case 3: launch_router_fwd_u<XDT, ODT, 3>(blocks, st, x, p, o, t, h); break;
-    default: launch_router_fwd_u<XDT, ODT, 4>(blocks, st, x, p, o, t, h); break;
+    switch (pl.U) {
+    case 1: launch_router_fwd_u<XDT, ODT, 1>(pl.blocks, st, x, p, o, t, h, pl.spans); break;
+    case 2: launch_router_fwd_u<XDT, ODT, 2>(pl.blocks, st, x, p, o, t, h, pl.spans); break;
+    case 3: launch_router_fwd_u<XDT, ODT, 3>(pl.blocks, st, x, p, o, t, h, pl.spans); break;
+    default: launch_router_fwd_u<XDT, ODT, 4>(pl.blocks, st, x, p, o, t, h, pl.spans); break;
     }
 }
 
 template <int XDT, int ODT, int U>
 void launch_router_bwd_u(int blocks, hipStream_t st, const void *g, const void *x, const float *p, void *gx,
-                         float *gp, int t, int h)
+                         float *gp, int t, int h, int spans)
 {
     hipLaunchKernelGGL((router_weight_bwd_kernel<XDT, ODT, U>), dim3(blocks), dim3(kBlock), 0, st,
                        static_cast<const char *>(g), static_cast<const char *>(x), p,
-                       static_cast<char *>(gx), gp, t, h);
+                       static_cast<char *>(gx), gp, t, h, spans);
 }
 
 template <int XDT, int ODT>
-void launch_router_bwd(int U, int blocks, hipStream_t st, const void *g, const void *x, const float *p,
+void launch_router_bwd(const RouterPlan &pl, hipStream_t st, const void *g, const void *x, const float *p,
                        void *gx, float *gp, int t, int h)
 {
-    switch (U) {
-    case 1: launch_router_bwd_u<XDT, ODT, 1>(blocks, st, g, x, p, gx, gp, t, h); break;
-    case 2: launch_router_bwd_u<XDT, ODT, 2>(blocks, st, g, x, p, gx, gp, t, h); break;
-    case 3: launch_router_bwd_u<XDT, ODT, 3>(blocks, st, g, x, p, gx, gp, t, h); break;
-    default: launch_router_bwd_u<XDT, ODT, 4>(blocks, st, g, x, p, gx, gp, t, h); break;
+    switch (pl.U) {
+    case 1: launch_router_bwd_u<XDT, ODT, 1>(pl.blocks, st, g, x, p, gx, gp, t, h, pl.spans); break;
+    case 2: launch_router_bwd_u<XDT, ODT, 2>(pl.blocks, st, g, x, p, gx, gp, t, h, pl.spans); break;
+    case 3: launch_router_bwd_u<XDT, ODT, 3>(pl.blocks, st, g, x, p, gx, gp, t, h, pl.spans); break;
+    default: launch_router_bwd_u<XDT, ODT, 4>(pl.blocks, st, g, x, p, gx, gp, t, h, pl.spans); break;
     }
 }
 
@@ -1049,15 +1121,13 @@ moe_status_t moe_router_weight_fwd(const void *x, moe_dtype_t x_dtype, const flo
     hipError_t he = device_cus(&cus);
     if (he != hipSuccess)
         return fail_hip(he);
-    const int U = pick_u(hidden / 8);
-    const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : split_walk_workgroups(tokens, row_chunks(hidden / 8, U), cus, 1);
+    const RouterPlan pl = plan_router(tokens, hidden, cus, num_workgroups, false);
     const int t = (int)tokens, h = (int)hidden;
-    if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_BF16>(U, blocks, stream, x, probs, out, t, h);
-    else if (x_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_F32>(U, blocks, stream, x, probs, out, t, h);
-    else if (x_dtype == MOE_FP16 && out_dtype == MOE_FP16) launch_router_fwd<DT_F16, DT_F16>(U, blocks, stream, x, probs, out, t, h);
-    else if (x_dtype == MOE_FP16) launch_router_fwd<DT_F16, DT_F32>(U, blocks, stream, x, probs, out, t, h);
-    else launch_router_fwd<DT_F32, DT_F32>(U, blocks, stream, x, probs, out, t, h);
+    if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_BF16>(pl, stream, x, probs, out, t, h);
+    else if (x_dtype == MOE_BF16) launch_router_fwd<DT_BF16, DT_F32>(pl, stream, x, probs, out, t, h);
+    else if (x_dtype == MOE_FP16 && out_dtype == MOE_FP16) launch_router_fwd<DT_F16, DT_F16>(pl, stream, x, probs, out, t, h);
+    else if (x_dtype == MOE_FP16) launch_router_fwd<DT_F16, DT_F32>(pl, stream, x, probs, out, t, h);
+    else launch_router_fwd<DT_F32, DT_F32>(pl, stream, x, probs, out, t, h);
     return launched();
 }
 
@@ -1094,15 +1164,13 @@ moe_status_t moe_router_weight_bwd(const void *grad_out, moe_dtype_t out_dtype, 
     hipError_t he = device_cus(&cus);
     if (he != hipSuccess)
         return fail_hip(he);
-    const int U = pick_u(hidden / 8);
-    const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : split_walk_workgroups(tokens, row_chunks(hidden / 8, U), cus, 1);
+    const RouterPlan pl = plan_router(tokens, hidden, cus, num_workgroups, true);
     const int t = (int)tokens, h = (int)hidden;
-    if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_BF16>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
-    else if (x_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
-    else if (x_dtype == MOE_FP16 && out_dtype == MOE_FP16) launch_router_bwd<DT_F16, DT_F16>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
-    else if (x_dtype == MOE_FP16) launch_router_bwd<DT_F16, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
-    else launch_router_bwd<DT_F32, DT_F32>(U, blocks, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_BF16>(pl, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else if (x_dtype == MOE_BF16) launch_router_bwd<DT_BF16, DT_F32>(pl, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else if (x_dtype == MOE_FP16 && out_dtype == MOE_FP16) launch_router_bwd<DT_F16, DT_F16>(pl, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else if (x_dtype == MOE_FP16) launch_router_bwd<DT_F16, DT_F32>(pl, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
+    else launch_router_bwd<DT_F32, DT_F32>(pl, stream, grad_out, x, probs, grad_x, grad_probs, t, h);
     return launched();
 }
 

@@ -99,8 +99,9 @@ ROUTER_TYPES = [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32"
 
 
 @pytest.mark.parametrize("x_dt,out_dt", ROUTER_TYPES)
-@pytest.mark.parametrize("tokens,hidden", [(1, 8), (333, 520), (1027, 2048), (64, 7168 + 8)])
+@pytest.mark.parametrize("tokens,hidden", [(1, 8), (333, 520), (1027, 2048), (64, 7168 + 8), (96, 7168)])
 def test_router_weight(x_dt, out_dt, tokens, hidden):
+    """7168 columns: the backward's waves take quarter rows (one masked chunk each)."""
     rng = np.random.default_rng(tokens + hidden)
     x = _rand((tokens, hidden), x_dt, rng, 3.0, specials=False)
     g = _rand((tokens, hidden), out_dt, rng, 1.0, specials=False)
@@ -123,8 +124,10 @@ def test_router_weight(x_dt, out_dt, tokens, hidden):
 @pytest.mark.parametrize("hidden", [5120, 7168, 8192])
 def test_router_weight_rows_split_over_waves(hidden):
     """Rows of 4 or more column chunks are shared by a workgroup's four waves (5, 7 and 4
-    chunks here): the probability gradient adds the waves' partials in wave order, so
-    every grid gives the same bits; outputs requested alone take the same paths."""
+    chunks here). The forward splits the chunks; where they do not divide by four (5120,
+    7168) the backward's waves take quarter rows instead. The probability gradient adds
+    the waves' partials in wave order, so every grid gives the same bits; outputs
+    requested alone take the same paths."""
     rng = np.random.default_rng(hidden)
     tokens = 777
     x = _rand((tokens, hidden), "bf16", rng, 3.0, specials=False)

@@ -17,7 +17,8 @@ Printed JSON line (stdout):
                it was taken on the current kernel source, else null
   cold         the same kernels timed one launch at a time after a read of an unrelated
                1 GiB buffer (evicts the 256 MB Infinity Cache without leaving dirty
-               lines), so no input can come from the previous launch's cache state
+               lines), so no input can come from the previous launch's cache state;
+               median and minimum of --cold-reps launches (default 30)
   hbm_probe    plain streaming kernels (1:1 copy, 2:1 and 3:2 read:write) moving the
                same bytes as fwd / bwd: the practical ceiling on this device
   cpu_baseline the CPU oracle (test infrastructure, untuned) on the same inputs,
@@ -149,7 +150,7 @@ class TimingEvents:
 def time_kernels(kernels, steps, warmup, cold_reps):
     """kernels: list of (name, launch), one step being each launched once in order.
     Returns wall ms per step, per-kernel event times (lists, ms) over the timed steps,
-    and cold medians (ms) per kernel (empty when cold_reps is 0).
+    and cold (median, min) ms per kernel (empty when cold_reps is 0).
 
     One event is recorded before the first launch and one after every launch, on the
     launch stream, so each launch lies between two events and consecutive launches
@@ -190,7 +191,7 @@ def time_kernels(kernels, steps, warmup, cold_reps):
                 torch.cuda.synchronize()
                 ts.append(ev.elapsed_ms(0, 1))
             ev.close()
-            cold[name] = float(np.median(ts))
+            cold[name] = (float(np.median(ts)), float(np.min(ts)))
         del evict
     return wall, per, cold
 
@@ -256,8 +257,10 @@ def bench_moe(args) -> int:
                       "GB/s": round(nbytes[name] / (avg * 1e6), 1),
                       "frac_of_peak": round(nbytes[name] / (avg * 1e6) / HBM_PEAK_GBS, 4)}
         if name in cold:
-            kern[name]["cold_us"] = round(cold[name] * 1e3, 2)
-            kern[name]["cold_GB/s"] = round(nbytes[name] / (cold[name] * 1e6), 1)
+            med, low = cold[name]
+            kern[name]["cold_us"] = round(med * 1e3, 2)
+            kern[name]["cold_us_min"] = round(low * 1e3, 2)
+            kern[name]["cold_GB/s"] = round(nbytes[name] / (med * 1e6), 1)
         log(f"{op} {name}: {kern[name]}")
     dom = max(nbytes, key=nbytes.get)
     traffic = measured_traffic(op, dom, os.path.join(ROOT, "profiles", f"pmc_moe_{op}.json"), MOE_SRC)
@@ -324,8 +327,9 @@ def main() -> int:
                          "elementwise operations next to it, at the headline MoE shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
-    ap.add_argument("--cold-reps", type=int, default=10,
-                    help="launches of each kernel timed after a cache-evicting read (0 = skip)")
+    ap.add_argument("--cold-reps", type=int, default=30,
+                    help="launches of each kernel timed one at a time, each after a cache-evicting "
+                         "read; their median and minimum are reported (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--fwd-workgroups", type=int, default=0)
@@ -385,10 +389,12 @@ def main() -> int:
 
     cold = None
     if args.cold_reps > 0:
-        cfm, cbm = cold_ms["fwd"], cold_ms["bwd"]
-        cold = {"fwd_us": round(cfm * 1e3, 2), "fwd_GB/s": round(fwd_bytes / (cfm * 1e6), 1),
-                "bwd_us": round(cbm * 1e3, 2), "bwd_GB/s": round(bwd_bytes / (cbm * 1e6), 1),
-                "reps": args.cold_reps, "statistic": "median"}
+        (cfm, cfl), (cbm, cbl) = cold_ms["fwd"], cold_ms["bwd"]
+        cold = {"fwd_us": round(cfm * 1e3, 2), "fwd_us_min": round(cfl * 1e3, 2),
+                "fwd_GB/s": round(fwd_bytes / (cfm * 1e6), 1),
+                "bwd_us": round(cbm * 1e3, 2), "bwd_us_min": round(cbl * 1e3, 2),
+                "bwd_GB/s": round(bwd_bytes / (cbm * 1e6), 1),
+                "reps": args.cold_reps, "statistic": "median (GB/s from the median)"}
         log(f"cold: fwd {cold['fwd_GB/s']} GB/s, bwd {cold['bwd_GB/s']} GB/s")
 
     probe = None

@@ -108,11 +108,23 @@ class TimingEvents:
 
     DISABLE_SYSTEM_FENCE = 0x20000000
 
+    @staticmethod
+    def _loaded_runtime() -> str:
+        """Path of the HIP runtime already mapped into this process (the one torch uses):
+        opening that same file returns the loaded library, never a second copy."""
+        with open("/proc/self/maps") as f:
+            for line in f:
+                fields = line.split()
+                if len(fields) >= 6 and os.path.basename(fields[5]).startswith("libamdhip64.so"):
+                    return fields[5]
+        raise RuntimeError("the HIP runtime is not loaded in this process")
+
     def __init__(self, count: int):
         import ctypes
         import torch
+        torch.cuda.init()
         self._ct = ctypes
-        self._hip = hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip = hip = ctypes.CDLL(self._loaded_runtime())
         hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,

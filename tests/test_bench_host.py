@@ -1,6 +1,6 @@
 """bench.py's host-side contract, no GPU needed: it refuses more than one GPU with a
-message, and the kernel-source hash that keys the counter summaries ignores comments
-and whitespace but not code."""
+message, the kernel-source hash that keys the counter summaries ignores comments and
+whitespace but not code, and its timing events use the HIP runtime torch loaded."""
 import os
 import subprocess
 import sys
@@ -41,3 +41,11 @@ def test_traffic_needs_matching_workload_and_source(tmp_path):
     p.write_text(json.dumps({"workload": "headline", "kernel_source_sha256_16": "0" * 16,
                              "bwd": {"hbm_bytes_per_launch": 123}}))
     assert bench.measured_traffic("headline", path=str(p)) is None
+
+
+def test_timing_events_use_the_loaded_hip_runtime():
+    """The bench's timing events go through the HIP runtime torch already mapped, found
+    in this process's mappings, so no second runtime is ever loaded beside it."""
+    import torch  # noqa: F401  (maps the HIP runtime)
+    path = bench.TimingEvents._loaded_runtime()
+    assert os.path.basename(path).startswith("libamdhip64.so") and os.path.exists(path)

@@ -11,7 +11,8 @@
  * counters (FETCH_SIZE / WRITE_SIZE) against a known size.
  *
  * Pointers: device memory on the current HIP device, 16-byte aligned, caller-owned,
- * destinations must not overlap sources. 1 <= n_src <= 3, 1 <= n_dst <= 2.
+ * destinations must not overlap sources. 1 <= n_src <= 3, 1 <= n_dst <= 2,
+ * 0 <= n_vec <= 2^44.
  * num_workgroups = 0 launches one wave per 4 KiB block (at most 16,777,215
  * workgroups), the activation kernels' default grid for short rows; an explicit
  * count must not exceed 16,777,215. Accesses are 128-bit buffer loads/stores with the

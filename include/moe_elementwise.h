@@ -43,13 +43,24 @@ extern "C" {
 
 #define MOE_ELEMENTWISE_ABI_VERSION 1
 
-typedef enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype_t;
+/* The enums are int-sized. Compiled as C++ they take int as their fixed underlying
+ * type, so every int a C caller passes is a value of the type; the library rejects
+ * the ones it does not know (an enum without a fixed type would make loading such a
+ * value undefined in C++). */
+#ifdef __cplusplus
+#define MOE_ENUM_BASE : int
+#else
+#define MOE_ENUM_BASE
+#endif
 
-typedef enum moe_status {
+typedef enum moe_dtype MOE_ENUM_BASE { MOE_BF16 = 0, MOE_FP16 = 1, MOE_FP32 = 2 } moe_dtype_t;
+
+typedef enum moe_status MOE_ENUM_BASE {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size (negative; rows or
-                                 tokens above 2,143,289,343; hidden above 2^26), dtype,
-                                 scale or workgroup count, overlap */
+                                 tokens above 2,143,289,343; hidden above 2^26; more
+                                 than 2^48 residual-add elements), dtype, scale or
+                                 workgroup count, overlap */
     MOE_ERR_ALIGNMENT = 2,    /* misaligned pointer, or a row width not a multiple of 8 */
     MOE_ERR_HIP = 3           /* launch failed; see moe_elementwise_last_hip_error */
 } moe_status_t;
@@ -60,7 +71,7 @@ typedef enum moe_status {
  * activation dtype before the residual is added (in fp32, rounded once), so the
  * result is bit-identical to the two unfused adds. The backward passes the output
  * gradient unchanged to all three inputs and needs no kernel.
- *   num_elements: elements of each tensor (any count >= 0).
+ *   num_elements: elements of each tensor, 0 <= num_elements <= 2^48.
  *   dtype: MOE_BF16, MOE_FP16 or MOE_FP32, the same for all four tensors.
  *   output may be the same pointer as one of the inputs (in place); any other
  *   overlap is an error.

@@ -60,7 +60,17 @@ extern "C" {
 
 #define SWIGLU_PROBS_ABI_VERSION 1
 
-typedef enum swiglu_status {
+/* The status enum is int-sized. Compiled as C++ it takes int as its fixed underlying
+ * type, so any int a C caller passes (say to swiglu_probs_status_string) is a value
+ * of the type (an enum without a fixed type would make loading an unknown value
+ * undefined in C++). */
+#ifdef __cplusplus
+#define SWIGLU_ENUM_BASE : int
+#else
+#define SWIGLU_ENUM_BASE
+#endif
+
+typedef enum swiglu_status SWIGLU_ENUM_BASE {
     SWIGLU_OK = 0,
     /* a required pointer is NULL, rows < 0, inter <= 0, rows > 2,143,289,343,
      * inter > 2^28 (268,435,456), limit is NaN or <= 0, num_workgroups < 0 or

@@ -102,8 +102,9 @@ bool aligned16(const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 
 extern "C" int hbm_probe_stream(const void *const *src, int n_src, void *const *dst, int n_dst,
                                 int64_t n_vec, int num_workgroups, hipStream_t stream)
 {
+    // n_vec at most 2^44 (2^48 bytes per array): byte counts and offsets stay in 64 bits
     if (!src || !dst || n_src < 1 || n_src > 3 || n_dst < 1 || n_dst > 2 || n_vec < 0 ||
-        num_workgroups < 0 || num_workgroups > kMaxWorkgroups)
+        n_vec > (int64_t(1) << 44) || num_workgroups < 0 || num_workgroups > kMaxWorkgroups)
         return 1;
     if (n_vec == 0)
         return 0;

@@ -830,6 +830,9 @@ bool dtype_ok(moe_dtype_t d) { return d == MOE_BF16 || d == MOE_FP16 || d == MOE
 
 constexpr int64_t kMaxRows = 0x7fffffffLL - 64LL * 65536LL;
 constexpr int64_t kMaxHidden = 1LL << 26;  // a row stays under 2^32 bytes in fp32
+// Elements of one residual-add tensor: far past any device's memory, and small enough
+// that its byte count and every byte offset fit in 64-bit arithmetic.
+constexpr int64_t kMaxElements = 1LL << 48;
 
 // Octs per lane per chunk: the U in 1..4 that leaves the fewest idle lane slots in a
 // row's last chunk, ties to the larger U (7168 columns: U = 2, seven full chunks, not
@@ -1069,7 +1072,7 @@ moe_status_t moe_residual_add(const void *expert_output, const void *shared_expe
                               const void *residual, void *output, int64_t num_elements,
                               moe_dtype_t dtype, hipStream_t stream, int num_workgroups)
 {
-    if (num_elements < 0 || !dtype_ok(dtype) || bad_grid(num_workgroups))
+    if (num_elements < 0 || num_elements > kMaxElements || !dtype_ok(dtype) || bad_grid(num_workgroups))
         return MOE_ERR_INVALID_ARG;
     if (num_elements == 0)
         return MOE_OK;

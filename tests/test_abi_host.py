@@ -144,6 +144,8 @@ def test_probe_validation(built):
     d2 = (ctypes.c_void_p * 1)(A16 + 16)
     assert so.hbm_probe_stream(s, 1, d2, 1, 4, 0, None) == 1   # overlap
     assert so.hbm_probe_stream(s, 1, d, 1, 4, 1 << 24, None) == 1
+    assert so.hbm_probe_stream(s, 1, d, 1, (1 << 44) + 1, 0, None) == 1   # byte count past 2^48
+    assert so.hbm_probe_stream(s, 1, d, 1, 2 ** 63 - 1, 0, None) == 1
 
 
 def test_moe_validation():
@@ -158,6 +160,8 @@ def test_moe_validation():
     assert lib.moe_residual_add(None, b, c, d, 8, 0, None, 0) == 1
     assert lib.moe_residual_add(a, b, c, d, 8, 0, None, -1) == 1
     assert lib.moe_residual_add(a, b, c, d, 8, 0, None, 1 << 24) == 1     # past the dispatch limit
+    assert lib.moe_residual_add(a, b, c, d, (1 << 48) + 8, 0, None, 0) == 1  # past 2^48 elements
+    assert lib.moe_residual_add(a, b, c, d, 2 ** 63 - 1, 2, None, 0) == 1
     f = lib.moe_router_weight_fwd
     assert f(a, 0, b, c, 0, 0, 8, None, 0) == 0
     assert f(a, 0, b, c, 1, 4, 8, None, 0) == 1                           # out must be x's type or fp32

@@ -1,4 +1,5 @@
-"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer, no GPU needed.
+"""Host code under AddressSanitizer, UndefinedBehaviorSanitizer and ThreadSanitizer, no GPU
+needed.
 
 * The CPU oracle (plain C) is built with gcc and both sanitizers and driven over every
   function, small inputs with every special value and every row rule
@@ -7,8 +8,11 @@
   (hipcc, -Xarch_host before each -fsanitize=) and their argument checks driven from C
   (tests/sanitize/abi_drive.c): every call fails validation or has nothing to do, so
   nothing reaches the HIP runtime or a GPU.
-* A planted out-of-bounds write in a copy of the oracle must be reported, which shows
-  the instrumentation is live.
+* The oracle's row blocks run on POSIX threads; the same drive under ThreadSanitizer
+  checks that no two threads touch the same memory unordered.
+* A planted out-of-bounds write and a planted race (two threads' row blocks overlapping
+  by one row), each in a copy of the oracle, must be reported, which shows the
+  instrumentation is live.
 
 AddressSanitizer must be the first library a program loads, so these tests skip where
 the environment preloads a library of its own.
@@ -35,11 +39,11 @@ def _run(cmd, **kw):
     return subprocess.run(cmd, capture_output=True, text=True, env=ENV, **kw)
 
 
-def _build_oracle_drive(out, sources):
+def _build_oracle_drive(out, sources, flags=CFLAGS_SAN):
     gcc = shutil.which("gcc")
     if gcc is None:
         pytest.skip("no gcc")
-    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math", "-pthread", *CFLAGS_SAN,
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math", "-pthread", *flags,
            os.path.join(HERE, "oracle_drive.c"), *sources, "-lm", "-o", out]
     res = _run(cmd)
     assert res.returncode == 0, res.stderr[-3000:]
@@ -66,6 +70,33 @@ def test_a_planted_overrun_is_reported(tmp_path):
     res = _run([exe], timeout=300)
     assert res.returncode != 0
     assert "AddressSanitizer" in res.stderr and "heap-buffer-overflow" in res.stderr, res.stderr[-3000:]
+
+
+CFLAGS_TSAN = ["-fsanitize=thread", "-g", "-O1"]
+
+
+def test_oracle_threads_under_tsan(tmp_path):
+    exe = str(tmp_path / "oracle_drive_tsan")
+    _build_oracle_drive(exe, ORACLE_SOURCES, CFLAGS_TSAN)
+    res = _run([exe], timeout=300)
+    assert res.returncode == 0, (res.stdout + res.stderr)[-4000:]
+    assert "oracle sanitizer drive: ok" in res.stdout and "ThreadSanitizer" not in res.stderr
+
+
+def test_a_planted_race_is_reported(tmp_path):
+    """Let each thread's block of rows run one row into the next thread's (the last
+    block stays in range): two threads then write that row's outputs unordered, and
+    ThreadSanitizer must report it."""
+    src = open(ORACLE_SOURCES[0]).read()
+    needle = "blk[t].r1 = r + n;"
+    assert src.count(needle) == 1, "the planted race no longer matches the oracle source"
+    planted = tmp_path / "swiglu_oracle_planted.c"
+    planted.write_text(src.replace(needle, "blk[t].r1 = r + n + (t + 1 < threads);"))
+    exe = str(tmp_path / "oracle_drive_race")
+    _build_oracle_drive(exe, [str(planted), ORACLE_SOURCES[1]], CFLAGS_TSAN)
+    res = _run([exe], timeout=300)
+    assert res.returncode != 0
+    assert "ThreadSanitizer: data race" in res.stderr, res.stderr[-3000:]
 
 
 def test_abi_argument_checks_under_sanitizers(tmp_path):

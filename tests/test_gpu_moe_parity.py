@@ -94,6 +94,19 @@ def test_residual_add_autograd():
     assert all(torch.equal(t.grad, g) for t in x)
 
 
+def test_residual_add_full_size():
+    """6720 x 7168 bf16 (the MoE workload), default launch: every element, bitwise."""
+    from memory_bound_elementwise_amd.workloads import make_moe_inputs
+    inp = make_moe_inputs("residual_add", seed=0)
+    e, sh, r = inp["expert"], inp["shared"], inp["residual"]
+    say(f"[residual add full] {e.shape[0]}x{e.shape[1]}")
+    out = torch.empty(e.shape, dtype=torch.bfloat16, device=DEV)
+    moe_residual_add(_dev(e, "bf16"), _dev(sh, "bf16"), _dev(r, "bf16"), out)
+    torch.cuda.synchronize()
+    want = moe_oracle.get().residual_add(e, sh, r, "bf16")
+    assert _same(_host(out, "bf16"), want, "bf16")
+
+
 # ---------------------------------------------------------------------------
 ROUTER_TYPES = [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32"), ("f32", "f32")]
 
@@ -199,6 +212,32 @@ def test_router_weight_autograd_and_grid():
         assert torch.equal(o, outs[0][0]) and torch.equal(gp.view(torch.int32), outs[0][1].view(torch.int32))
 
 
+def test_router_weight_full_size_sampled():
+    """53760 x 7168 bf16 (the MoE workload), default launch (the backward's waves take
+    quarter rows): sampled rows against the oracle, forward and grad_x bitwise."""
+    from memory_bound_elementwise_amd.workloads import make_moe_inputs
+    inp = make_moe_inputs("router_weight", seed=0)
+    x, p, g = inp["x"], inp["probs"], inp["grad_out"]
+    tokens, hidden = x.shape
+    say(f"[router full] {tokens}x{hidden}")
+    xd, gd, dp = _dev(x, "bf16"), _dev(g, "bf16"), torch.from_numpy(p).to(DEV)
+    out = torch.empty_like(xd)
+    gx = torch.empty_like(xd)
+    gp = torch.full((tokens,), -7.0, device=DEV)
+    moe_router_weight_fwd(xd, dp, out)
+    moe_router_weight_bwd(gd, xd, dp, gx, gp)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(3), np.arange(tokens - 100, tokens),
+                                    np.random.default_rng(3).integers(0, tokens, 200)]))
+    ti = torch.from_numpy(idx).to(DEV)
+    orc = moe_oracle.get()
+    assert _same(_host(out[ti], "bf16"), orc.router_weight_fwd(x[idx], "bf16", p[idx], "bf16"), "bf16")
+    ref = orc.router_weight_bwd(g[idx], "bf16", x[idx], "bf16", p[idx])
+    assert _same(_host(gx[ti], "bf16"), ref["grad_x"], "bf16")
+    bad = grad_probs_violations(gp[ti].cpu().numpy(), ref["grad_probs_f64"], ref["row_scale"])
+    assert bad.size == 0, f"router grad_probs: {bad.size} rows off"
+
+
 # ---------------------------------------------------------------------------
 def _sq_run(x, p, **kw):
     rows, hidden = x.shape
@@ -252,6 +291,27 @@ def test_squared_relu_rows(zero_padding):
         want = moe_oracle.get().squared_relu_probs(x, p, **kw)
         assert_within_ulp(got, want, 1, f"rows n_used={n_used}")
         assert np.array_equal(got == 0xFFFF, want == 0xFFFF)
+
+
+@pytest.mark.parametrize("clamp_scale", [None, 4.0])
+def test_squared_relu_full_size_sampled(clamp_scale):
+    """53,760 x 2,048 (the MoE workload), default launch; sampled rows against the oracle."""
+    from memory_bound_elementwise_amd.workloads import make_moe_inputs
+    inp = make_moe_inputs("squared_relu", seed=0)
+    x, p = inp["x"], inp["probs"]
+    rows, hidden = x.shape
+    say(f"[sqrelu fwd full] s={clamp_scale} {rows}x{hidden}")
+    y = torch.empty((rows, hidden), dtype=torch.bfloat16, device=DEV)
+    moe_squared_relu_probs_fwd(_dev(x, "bf16"), torch.from_numpy(p).to(DEV), y, clamp_scale=clamp_scale)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(3), np.arange(rows - 200, rows),
+                                    np.random.default_rng(4).integers(0, rows, 300)]))
+    got = _host(y[torch.from_numpy(idx).to(DEV)], "bf16")
+    want = moe_oracle.get().squared_relu_probs(x[idx], p[idx], clamp_scale=clamp_scale)
+    if clamp_scale is None:
+        assert _same(got, want, "bf16")
+    else:
+        assert_within_ulp(got, want, 1, "full size")
 
 
 # ---------------------------------------------------------------------------

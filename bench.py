@@ -20,7 +20,9 @@ Printed JSON line (stdout):
                lines), so no input can come from the previous launch's cache state;
                median and minimum of --cold-reps launches (default 30)
   hbm_probe    plain streaming kernels (1:1 copy, 2:1 and 3:2 read:write) moving the
-               same bytes as fwd / bwd: the practical ceiling on this device
+               same bytes as fwd / bwd: the practical ceiling on this device. With --op,
+               the probe at each kernel's own read:write mix and size, and the kernel's
+               fraction of it. Median of five windows of 20 back-to-back launches
   cpu_baseline the CPU oracle (test infrastructure, untuned) on the same inputs,
                timed on this host's cores
 Progress goes to stderr.
@@ -205,7 +207,45 @@ def time_kernels(kernels, steps, warmup, cold_reps):
             ev.close()
             cold[name] = (float(np.median(ts)), float(np.min(ts)))
         del evict
+        torch.cuda.empty_cache()  # later buffers (the probe's) get memory of their own
     return wall, per, cold
+
+
+def time_probe(srcs, dsts, reps=20, warmup=20, windows=5):
+    """Average ms per launch of the streaming probe moving srcs -> dsts: `warmup` untimed
+    launches, then `windows` windows of `reps` back-to-back launches, each timed with
+    TimingEvents on the launch stream; the median window is returned.
+    Right after the cold leg's host-synchronised launches, one window of 20 launches
+    after 3 (or even 20) warm-up launches ran the residual add's 3:1 probe at 3.5-5.2
+    instead of 6.5 TB/s: the device takes a few milliseconds to return to full speed, so
+    a single short window can fall inside that."""
+    import numpy as np
+    import torch
+    from memory_bound_elementwise_amd.hbm_probe import hbm_probe_stream
+    for _ in range(warmup):
+        hbm_probe_stream(srcs, dsts)
+    ev = TimingEvents(windows + 1)
+    ev.record(0)
+    for w in range(windows):
+        for _ in range(reps):
+            hbm_probe_stream(srcs, dsts)
+        ev.record(w + 1)
+    torch.cuda.synchronize()
+    ms = [ev.elapsed_ms(w, w + 1) / reps for w in range(windows)]
+    ev.close()
+    return float(np.median(ms))
+
+
+# The streaming probe's mix for each MoE kernel: (arrays read, arrays written, bytes per
+# array), so that it moves the kernel's algorithmic bytes with its read:write ratio.
+def moe_probe_mix(op, inp):
+    if op == "residual_add":
+        return {"residual_add": (3, 1, inp["expert"].size * 2)}
+    if op in ("router_weight", "squared_relu"):
+        n = inp["x"].size * 2
+        return {"fwd": (1, 1, n), "bwd": (2, 1, n)}
+    im, hidden = inp["inverse_map"], inp["expert_output"].shape[1]
+    return {"unpermute": (2, 1, im.shape[0] * hidden * 4)}   # gathers about 2x the fp32 output
 
 
 def bench_moe(args) -> int:
@@ -277,6 +317,23 @@ def bench_moe(args) -> int:
     dom = max(nbytes, key=nbytes.get)
     traffic = measured_traffic(op, dom, os.path.join(ROOT, "profiles", f"pmc_moe_{op}.json"), MOE_SRC)
 
+    probe = None
+    if not args.no_probe:
+        probe = {}
+        for name, (ns, nd, arr) in moe_probe_mix(op, inp).items():
+            n16 = arr // 32 * 16  # whole 16-byte vectors, as int16 elements
+            bufs = [torch.ones(n16, dtype=torch.int16, device=dev) for _ in range(ns + nd)]
+            ms = time_probe(bufs[:ns], bufs[ns:])
+            moved = (ns + nd) * n16 * 2
+            gbs = moved / (ms * 1e6)
+            probe[name] = {"mix": f"{ns}:{nd}", "bytes": moved, "us": round(ms * 1e3, 2),
+                           "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                           "kernel_frac_of_probe": round(kern[name]["GB/s"] / gbs, 4)}
+            log(f"{op} probe for {name} ({ns}:{nd}): {probe[name]['GB/s']} GB/s; kernel at "
+                f"{probe[name]['kernel_frac_of_probe']:.3f} of it")
+            del bufs
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle.moe as mo
@@ -320,6 +377,7 @@ def bench_moe(args) -> int:
         "kernels": kern,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kern[dom]["frac_of_peak"], "traffic": traffic},
+        "hbm_probe": probe,
         "cpu_baseline": cpu,
     }), flush=True)
     return 0
@@ -411,7 +469,6 @@ def main() -> int:
 
     probe = None
     if not args.no_probe:
-        from memory_bound_elementwise_amd.hbm_probe import hbm_probe_stream
         probe = {}
         # same bytes per stream as the kernels: fwd = 2 reads of x/2 + 1 write; bwd = 3 + 2
         nvec_elems = (rows * inter) // 8 * 8
@@ -420,17 +477,7 @@ def main() -> int:
             b.fill_(1)
         for name, ns, nd in (("copy_1r1w", 1, 1), ("fwd_like_2r1w", 2, 1), ("bwd_like_3r2w", 3, 2)):
             srcs, dsts = bufs[:ns], bufs[3:3 + nd]
-            for _ in range(3):
-                hbm_probe_stream(srcs, dsts)
-            ev = TimingEvents(2)
-            reps = 20
-            ev.record(0)
-            for _ in range(reps):
-                hbm_probe_stream(srcs, dsts)
-            ev.record(1)
-            torch.cuda.synchronize()
-            ms = ev.elapsed_ms(0, 1) / reps
-            ev.close()
+            ms = time_probe(srcs, dsts)
             moved = (ns + nd) * nvec_elems * 2
             probe[name] = {"bytes": moved, "us": round(ms * 1e3, 2),
                            "GB/s": round(moved / (ms * 1e6), 1),

@@ -20,8 +20,11 @@ namespace {
 
 using namespace cdna4;
 
-constexpr int kU = 4;
-constexpr uint32_t kBlockBytes = kU * kWave * kVecBytes;  // 4 KiB per stream per block
+#ifndef HBM_PROBE_U
+#define HBM_PROBE_U 4
+#endif
+constexpr int kU = HBM_PROBE_U;  // 16-byte vectors per lane per stream per block
+constexpr uint32_t kBlockBytes = kU * kWave * kVecBytes;  // 4 KiB per stream per block at kU = 4
 
 struct Ptrs {
     const char *src[3];

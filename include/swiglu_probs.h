@@ -136,7 +136,8 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
 /* Workgroup count the library would launch for this call shape on the current
  * device (direction 0 = forward, 1 = backward), or -1 on error. Host only.
  * A row is cut into column chunks of U 16-byte vectors per lane (64 lanes): the
- * forward takes the U in 1..4 that leaves the fewest idle lanes, the backward cuts
+ * forward takes the U in 1..4 that leaves the fewest idle lanes (U = 2 for rows of
+ * exactly 4 vectors per lane, read as two pipelined chunks), the backward cuts
  * rows of 4 or more vectors per lane into 4 or more chunks. Rows of one or two
  * chunks get one wave per row, ceil(rows / 4) workgroups; rows of three chunks one
  * workgroup per CU, balanced; rows of four or more one workgroup per row, its four

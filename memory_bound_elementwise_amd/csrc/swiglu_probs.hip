@@ -15,8 +15,8 @@
 //     half, the up half and (backward) grad_y: every access is 128 bits wide and one
 //     wave instruction covers 1 KiB of contiguous memory. A row is processed in
 //     chunks of U vectors per lane: the forward takes the U that leaves the fewest
-//     idle lanes, the backward cuts rows of 4 or more vectors per lane into 4 or more
-//     chunks. Rows of 4 or more chunks are shared by a workgroup's four waves, a
+//     idle lanes (two chunks of 2 for rows of exactly 4 vectors per lane), the backward
+//     cuts rows of 4 or more vectors per lane into 4 or more chunks. Rows of 4 or more chunks are shared by a workgroup's four waves, a
 //     quarter of the chunks each (walk_row_split); shorter rows go one per wave
 //     (walk_rows).
 //   * Every load and store is a buffer instruction on a per-row buffer resource
@@ -337,13 +337,25 @@ int64_t chunks_per_row(int64_t vpr, int U) { return (vpr + (int64_t)U * kWave - 
 // gives 4 or more chunks, so the workgroup's four waves share each row; else pick_u.
 // Measured against pick_u's width at 53760 x 2048: 171 against 176 us; 26880 x 4096:
 // 172 against 186 us; narrower rows are unaffected. (The forward measured faster with
-// whole rows per wave, 103 against 111 us at 2048 columns, so it keeps pick_u.)
+// whole rows per wave, 103 against 111 us at 2048 columns, so it does not split rows.)
 int pick_u_bwd(int64_t vpr)
 {
     const int64_t u = (vpr + kWave - 1) / kWave;
     if (u >= kWavesPerBlock)
         return (int)(u / kWavesPerBlock > kMaxU ? kMaxU : u / kWavesPerBlock);
     return pick_u(vpr);
+}
+
+// The forward's chunk width: pick_u, except that a row of exactly 4 vectors per lane
+// (2,048 columns) is read as two chunks of 2, which the wave pipelines. 2 KiB per wave
+// per stream is what the plain streaming probe moves fastest at every read:write mix
+// on MI355X (2:1: 6,657 GB/s against 6,610 at 4 KiB); interleaved at 53760 x 2048 the
+// forward took 104.0 against 104.6 us. Other widths keep pick_u, whose chunks fit them
+// with fewer idle lanes.
+int pick_u_fwd(int64_t vpr)
+{
+    const int64_t u = (vpr + kWave - 1) / kWave;
+    return u == 4 && kMaxU >= 2 ? 2 : pick_u(vpr);
 }
 
 // Address ranges, for the check that no output overlaps an input.
@@ -442,7 +454,7 @@ swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint1
     if (e != hipSuccess)
         return fail_hip(e);
     const int vpr = (int)(inter / 8);
-    const int U = pick_u(vpr);
+    const int U = pick_u_fwd(vpr);
     const int blocks = num_workgroups > 0 ? num_workgroups
                                           : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
                                                                   info->fwd_blocks_per_cu[U]);
@@ -534,7 +546,7 @@ int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter)
     DeviceLaunchInfo *info = nullptr;
     if (device_info(&info) != hipSuccess)
         return -1;
-    const int U = direction == 0 ? pick_u(inter / 8) : pick_u_bwd(inter / 8);
+    const int U = direction == 0 ? pick_u_fwd(inter / 8) : pick_u_bwd(inter / 8);
     const int bpc = direction == 0 ? info->fwd_blocks_per_cu[U] : info->bwd_blocks_per_cu[U];
     return split_walk_workgroups(rows, chunks_per_row(inter / 8, U), info->cus, bpc);
 }

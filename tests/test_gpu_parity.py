@@ -117,7 +117,7 @@ def test_default_workgroups():
     per row, its four waves sharing the row's chunks. Never past the dispatch limit."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = WORKLOADS["headline"].rows
-    # forward: pick_u's width; 2048 columns = 1 chunk, 6144 = 3 chunks, 8192 = 4 chunks
+    # forward: 2048 columns = 2 chunks of 2 (one wave per row), 6144 = 3 chunks, 8192 = 4 chunks
     wg = swiglu_probs_default_workgroups("fwd", rows, WORKLOADS["headline"].inter)
     say(f"[launch] fwd inter {WORKLOADS['headline'].inter}: {wg} workgroups")
     assert wg == -(-rows // 4)

@@ -6,25 +6,37 @@ inputs of a workload (default: the 1.1 GB "headline" shape, rows 53760, inter
 2048), already resident in HBM. W untimed warm-up steps, then K timed steps
 bracketed by device synchronisation.
 
+Order of the legs: the streaming ceilings, the timed steps, each kernel back to back,
+the cold launches, the CPU baseline. The ceilings come first so that a device which sat
+idle while the inputs were drawn has left its clock ramp before the timed steps.
+
 Printed JSON line (stdout):
-  value        whole-job algorithmic GB/s = (fwd + bwd algorithmic bytes) / step time
-  fwd, bwd     per-kernel average duration from HIP events on the launch stream,
-               one before the first launch and one after every launch (each launch
-               lies between two), and the GB/s and HBM fraction they give
+  value        whole-job algorithmic GB/s = (fwd + bwd algorithmic bytes) / wall time per
+               timed step (ms_per_step; device_ms_per_step is the same from two stream
+               events around the timed steps, with none between the kernels)
+  fwd, bwd     per-kernel duration over K more steps run right after the timed ones, in
+               which each launch records its own start and end into a pair of events
+               (the library's timed entry points, hipExtLaunchKernel): the kernel alone;
+               average, min, max, and the GB/s and HBM fraction the average gives. us_back_to_back: the kernel alone, launched
+               back to back (median of five windows of 20 launches between one pair of
+               stream events); frac_of_best_ceiling: its GB/s over the best ceiling
+               measured at its read:write mix
   roofline     for the dominant kernel (the backward): algorithmic bytes per launch /
                its average duration, against the 8 TB/s MI355X HBM peak; traffic =
-               HBM bytes per launch from the committed rocprofv3 counter summary when
-               it was taken on the current kernel source, else null
-  cold         the same kernels timed one launch at a time after a read of an unrelated
-               1 GiB buffer (evicts the 256 MB Infinity Cache without leaving dirty
-               lines), so no input can come from the previous launch's cache state;
-               median and minimum of --cold-reps launches (default 30)
-  hbm_probe    plain streaming kernels (1:1 copy, 2:1 and 3:2 read:write) moving the
-               same bytes as fwd / bwd: the practical ceiling on this device. With --op,
-               the probe at each kernel's own read:write mix and size, and the kernel's
-               fraction of it. Median of five windows of 20 back-to-back launches
+               HBM bytes per launch from the committed rocprofv3 counter summary, and
+               trace_us the average from the committed rocprofv3 kernel trace, each when
+               it was taken on the current kernel source (else null / absent)
+  cold         the same kernels one launch at a time after a read of an unrelated 1 GiB
+               buffer (evicts the 256 MB Infinity Cache without leaving dirty lines), so
+               no input can come from the previous launch's cache state; median and
+               minimum of --cold-reps launches (default 30)
+  hbm_probe    streaming ceilings at the same bytes: the in-repo probe (1:1 copy, 2:1 and
+               3:2 read:write) and, sharing no code with the kernels, torch copy_, a bf16
+               torch.add and hipMemcpyDtoDAsync. With --op, the probe at each kernel's
+               own read:write mix and size, and the kernel's fraction of it
   cpu_baseline the CPU oracle (test infrastructure, untuned) on the same inputs,
-               timed on this host's cores
+               timed on this host's cores (cores = threads used, host_cores = the
+               process's CPU affinity)
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -79,6 +91,23 @@ def measured_traffic(workload: str, key: str = "bwd", path: str = COUNTERS, sour
     return d.get(key, {}).get("hbm_bytes_per_launch")
 
 
+TRACE = os.path.join(ROOT, "profiles", "trace_swiglu_probs_headline.json")
+
+
+def trace_average(workload: str, key: str = "bwd", path: str = TRACE):
+    """Average kernel duration (us) of kernel `key` over the timed launches of the committed
+    rocprofv3 kernel trace of this bench, or None when it is missing, for another workload,
+    or taken on other kernel sources."""
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("workload") != workload or d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get(key, {}).get("average_us")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -99,6 +128,9 @@ MOE_OPS = {
 }
 
 
+DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+
 class TimingEvents:
     """HIP events for timing only, on torch's current stream of cuda:0 (the stream the
     kernels are launched on). They are created with hipEventDisableSystemFence: recording
@@ -107,8 +139,6 @@ class TimingEvents:
     orders everything). On MI355X that took a fwd+bwd step with two events from 281.6 to
     278.0 us (275.0 with none). torch's Event cannot be given the flag, so this calls
     the HIP runtime torch has loaded."""
-
-    DISABLE_SYSTEM_FENCE = 0x20000000
 
     @staticmethod
     def _loaded_runtime() -> str:
@@ -121,7 +151,7 @@ class TimingEvents:
                     return fields[5]
         raise RuntimeError("the HIP runtime is not loaded in this process")
 
-    def __init__(self, count: int):
+    def __init__(self, count: int, flags: int = DISABLE_SYSTEM_FENCE):
         import ctypes
         import torch
         torch.cuda.init()
@@ -136,11 +166,15 @@ class TimingEvents:
         self._ev = []
         for _ in range(count):
             e = ctypes.c_void_p()
-            rc = hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            rc = hip.hipEventCreateWithFlags(ctypes.byref(e), flags)
             if rc != 0:
                 self.close()
                 raise RuntimeError(f"hipEventCreateWithFlags failed: hipError_t {rc}")
             self._ev.append(e)
+
+    def handle(self, i: int) -> int:
+        """The hipEvent_t of event i, for a launch that records into it."""
+        return self._ev[i].value
 
     def record(self, i: int) -> None:
         rc = self._hip.hipEventRecord(self._ev[i], self._stream)
@@ -211,29 +245,141 @@ def time_kernels(kernels, steps, warmup, cold_reps):
     return wall, per, cold
 
 
-def time_probe(srcs, dsts, reps=20, warmup=20, windows=5):
-    """Average ms per launch of the streaming probe moving srcs -> dsts: `warmup` untimed
-    launches, then `windows` windows of `reps` back-to-back launches, each timed with
-    TimingEvents on the launch stream; the median window is returned.
-    Right after the cold leg's host-synchronised launches, one window of 20 launches
-    after 3 (or even 20) warm-up launches ran the residual add's 3:1 probe at 3.5-5.2
-    instead of 6.5 TB/s: the device takes a few milliseconds to return to full speed, so
-    a single short window can fall inside that."""
+def time_windows(fn, reps=20, warmup=20, windows=5):
+    """Average ms per launch of fn: `warmup` untimed launches, then `windows` windows of
+    `reps` back-to-back launches, each window timed with TimingEvents on the launch
+    stream; the median window is returned. Right after host-synchronised work one window
+    of 20 launches after 3 (or even 20) warm-up launches ran the residual add's 3:1 probe
+    at 3.5-5.2 instead of 6.5 TB/s: the device takes a few milliseconds to return to
+    full speed, so a single short window can fall inside that."""
     import numpy as np
     import torch
-    from memory_bound_elementwise_amd.hbm_probe import hbm_probe_stream
     for _ in range(warmup):
-        hbm_probe_stream(srcs, dsts)
+        fn()
     ev = TimingEvents(windows + 1)
     ev.record(0)
     for w in range(windows):
         for _ in range(reps):
-            hbm_probe_stream(srcs, dsts)
+            fn()
         ev.record(w + 1)
     torch.cuda.synchronize()
     ms = [ev.elapsed_ms(w, w + 1) / reps for w in range(windows)]
     ev.close()
     return float(np.median(ms))
+
+
+def time_probe(srcs, dsts, reps=20, warmup=20, windows=5):
+    """time_windows of the streaming probe moving srcs -> dsts."""
+    from memory_bound_elementwise_amd.hbm_probe import hbm_probe_stream
+    return time_windows(lambda: hbm_probe_stream(srcs, dsts), reps, warmup, windows)
+
+
+def streaming_ceilings(n_elems, dev):
+    """The device's streaming ceilings at the activation's byte counts: the in-repo probe
+    at 1:1, 2:1 and 3:2 read:write, and, as ceilings that share no code with the kernels,
+    torch's own copy_ (1:1) and bf16 add (2:1) and hipMemcpyDtoDAsync (1:1), each over
+    arrays of n_elems bf16 elements (as large as one half of x). Every figure is
+    time_windows' median window; GB/s counts the bytes each call reads and writes."""
+    import ctypes
+    import torch
+    bufs = [torch.empty(n_elems, dtype=torch.bfloat16, device=dev) for _ in range(5)]
+    for b in bufs:
+        b.fill_(1)
+    i16 = [b.view(torch.int16) for b in bufs]
+    nbytes = n_elems * 2
+    hip = ctypes.CDLL(TimingEvents._loaded_runtime())
+    hip.hipMemcpyDtoDAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(0).cuda_stream)
+
+    def memcpy():
+        rc = hip.hipMemcpyDtoDAsync(bufs[3].data_ptr(), bufs[0].data_ptr(), nbytes, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyDtoDAsync failed: hipError_t {rc}")
+
+    from memory_bound_elementwise_amd.hbm_probe import hbm_probe_stream
+    cases = [
+        ("copy_1r1w", "in-repo probe", lambda: hbm_probe_stream(i16[:1], i16[3:4]), 2),
+        ("fwd_like_2r1w", "in-repo probe", lambda: hbm_probe_stream(i16[:2], i16[3:4]), 3),
+        ("bwd_like_3r2w", "in-repo probe", lambda: hbm_probe_stream(i16[:3], i16[3:5]), 5),
+        ("torch_copy_1r1w", "torch Tensor.copy_", lambda: bufs[3].copy_(bufs[0]), 2),
+        ("torch_add_2r1w", "torch.add (bf16)", lambda: torch.add(bufs[0], bufs[1], out=bufs[3]), 3),
+        ("hip_memcpy_1r1w", "hipMemcpyDtoDAsync", memcpy, 2),
+    ]
+    out = {}
+    for name, kind, fn, arrays in cases:
+        ms = time_windows(fn)
+        moved = arrays * nbytes
+        out[name] = {"kind": kind, "bytes": moved, "us": round(ms * 1e3, 2),
+                     "GB/s": round(moved / (ms * 1e6), 1),
+                     "frac_of_peak": round(moved / (ms * 1e6) / HBM_PEAK_GBS, 4)}
+        log(f"ceiling {name} ({kind}): {out[name]['GB/s']} GB/s")
+    del bufs, i16
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_launches(kernels, steps, warmup):
+    """kernels: list of (name, launch); launch(events) enqueues one kernel and, given a
+    (start, stop) pair of event handles, has the launch itself record the kernel's start
+    and end into them (the library's timed entry points).
+
+    `warmup` untimed steps (each kernel once, in order), then the timed region: `steps`
+    steps bracketed by device synchronisation, with no event between the kernels (two
+    stream events bracket the whole region), giving the wall and the device ms per step.
+    Then `steps` more steps in which every launch records its own start and end, giving
+    each kernel's durations. Those events cost the stream about 7 us per launch on
+    MI355X (a step took 283 against 272 us), so they stay out of the step timing.
+    Returns (wall ms per step, device ms per step, {name: [ms per launch]})."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in kernels:
+            fn(None)
+    torch.cuda.synchronize()
+    sev = TimingEvents(2)
+    t0 = time.perf_counter()
+    sev.record(0)
+    for _ in range(steps):
+        for _, fn in kernels:
+            fn(None)
+    sev.record(1)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    dev_ms = sev.elapsed_ms(0, 1) / steps
+    sev.close()
+    n = len(kernels)
+    kev = TimingEvents(2 * n * steps, flags=0)
+    for s in range(steps):
+        for i, (_, fn) in enumerate(kernels):
+            k = 2 * (s * n + i)
+            fn((kev.handle(k), kev.handle(k + 1)))
+    torch.cuda.synchronize()
+    per = {name: [kev.elapsed_ms(2 * (s * n + i), 2 * (s * n + i) + 1) for s in range(steps)]
+           for i, (name, _) in enumerate(kernels)}
+    kev.close()
+    return wall, dev_ms, per
+
+
+def time_cold(kernels, reps):
+    """Each kernel alone, `reps` times, each launch after a read of an unrelated 1 GiB
+    buffer (evicts the 256 MB Infinity Cache without leaving dirty lines), timed by the
+    launch's own start and end events. (median, min) ms per kernel."""
+    import numpy as np
+    import torch
+    evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+    cold = {}
+    for name, fn in kernels:
+        ts = []
+        ev = TimingEvents(2, flags=0)
+        for _ in range(reps):
+            evict.sum(dtype=torch.int64)
+            fn((ev.handle(0), ev.handle(1)))
+            torch.cuda.synchronize()
+            ts.append(ev.elapsed_ms(0, 1))
+        ev.close()
+        cold[name] = (float(np.median(ts)), float(np.min(ts)))
+    del evict
+    torch.cuda.empty_cache()
+    return cold
 
 
 # The streaming probe's mix for each MoE kernel: (arrays read, arrays written, bytes per
@@ -298,6 +444,22 @@ def bench_moe(args) -> int:
         shape = {"tokens": im.shape[0], "local_experts": im.shape[1], "hidden": eo.shape[1],
                  "routed_pairs": int((inp["inverse_map"] >= 0).sum())}
 
+    # the probe first: see main() (it also brings an idle device out of its clock ramp)
+    probe = None
+    if not args.no_probe:
+        probe = {}
+        for name, (ns, nd, arr) in moe_probe_mix(op, inp).items():
+            n16 = arr // 32 * 16  # whole 16-byte vectors, as int16 elements
+            bufs = [torch.ones(n16, dtype=torch.int16, device=dev) for _ in range(ns + nd)]
+            ms = time_probe(bufs[:ns], bufs[ns:])
+            moved = (ns + nd) * n16 * 2
+            gbs = moved / (ms * 1e6)
+            probe[name] = {"mix": f"{ns}:{nd}", "bytes": moved, "us": round(ms * 1e3, 2),
+                           "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"{op} probe for {name} ({ns}:{nd}): {probe[name]['GB/s']} GB/s")
+            del bufs
+        torch.cuda.empty_cache()
+
     log(f"{op}: warm-up {args.warmup}, timing {args.steps} steps")
     wall, per, cold = time_kernels(kernels, args.steps, args.warmup, args.cold_reps)
     total = sum(nbytes.values())
@@ -317,22 +479,10 @@ def bench_moe(args) -> int:
     dom = max(nbytes, key=nbytes.get)
     traffic = measured_traffic(op, dom, os.path.join(ROOT, "profiles", f"pmc_moe_{op}.json"), MOE_SRC)
 
-    probe = None
-    if not args.no_probe:
-        probe = {}
-        for name, (ns, nd, arr) in moe_probe_mix(op, inp).items():
-            n16 = arr // 32 * 16  # whole 16-byte vectors, as int16 elements
-            bufs = [torch.ones(n16, dtype=torch.int16, device=dev) for _ in range(ns + nd)]
-            ms = time_probe(bufs[:ns], bufs[ns:])
-            moved = (ns + nd) * n16 * 2
-            gbs = moved / (ms * 1e6)
-            probe[name] = {"mix": f"{ns}:{nd}", "bytes": moved, "us": round(ms * 1e3, 2),
-                           "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                           "kernel_frac_of_probe": round(kern[name]["GB/s"] / gbs, 4)}
-            log(f"{op} probe for {name} ({ns}:{nd}): {probe[name]['GB/s']} GB/s; kernel at "
-                f"{probe[name]['kernel_frac_of_probe']:.3f} of it")
-            del bufs
-        torch.cuda.empty_cache()
+    if probe:
+        for name in probe:
+            probe[name]["kernel_frac_of_probe"] = round(kern[name]["GB/s"] / probe[name]["GB/s"], 4)
+            log(f"{op} {name}: kernel at {probe[name]['kernel_frac_of_probe']:.3f} of its probe")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -372,7 +522,7 @@ def bench_moe(args) -> int:
         "metric": f"achieved HBM GB/s of the {MOE_OPS[op]} and % of MI355X HBM peak",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"moe_{op}", **shape, "io_dtype": "bf16", "seed": 0},
         "kernels": kern,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS,
@@ -431,6 +581,15 @@ def main() -> int:
     inp = make_inputs(w, seed=0)
     rows, two_inter = inp["x"].shape
     inter = two_inter // 2
+
+    # The ceilings first: besides giving the practical ceiling, their ~0.1 s of streaming
+    # brings a device that sat idle while the inputs were drawn out of its clock ramp
+    # (after idling, the shader clock needs some 10-30 ms of load to settle; launches
+    # timed inside that run up to 20% slow).
+    probe = None
+    if not args.no_probe:
+        probe = streaming_ceilings((rows * inter) // 8 * 8, dev)
+
     x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
     gy = torch.from_numpy(inp["grad_y"].view(np.int16)).to(dev)
     probs = torch.from_numpy(inp["probs"]).to(dev)
@@ -443,47 +602,47 @@ def main() -> int:
     L = inp["limit"]
     fwd_bytes = algorithmic_bytes(w, "fwd")
     bwd_bytes = algorithmic_bytes(w, "bwd")
+    nbytes = {"fwd": fwd_bytes, "bwd": bwd_bytes}
 
     kernels = [
-        ("fwd", lambda: swiglu_probs_fwd(x, probs, y, L, num_workgroups=args.fwd_workgroups, **kw)),
-        ("bwd", lambda: swiglu_probs_bwd(x, probs, gy, gx, gp, L, num_workgroups=args.bwd_workgroups, **kw)),
+        ("fwd", lambda ev: swiglu_probs_fwd(x, probs, y, L, num_workgroups=args.fwd_workgroups, events=ev, **kw)),
+        ("bwd", lambda ev: swiglu_probs_bwd(x, probs, gy, gx, gp, L, num_workgroups=args.bwd_workgroups,
+                                            events=ev, **kw)),
     ]
     log(f"warm-up {args.warmup} steps, timing {args.steps} steps")
-    ms_per_step, per, cold_ms = time_kernels(kernels, args.steps, args.warmup, args.cold_reps)
-    fwd_ms, bwd_ms = per["fwd"], per["bwd"]
-    f_avg, b_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
-    f_gbs, b_gbs = fwd_bytes / (f_avg * 1e6), bwd_bytes / (b_avg * 1e6)
+    ms_per_step, dev_ms_per_step, per = time_launches(kernels, args.steps, args.warmup)
     value = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e6)
-    log(f"fwd {f_avg * 1e3:.1f} us ({f_gbs:.0f} GB/s), bwd {b_avg * 1e3:.1f} us ({b_gbs:.0f} GB/s), "
-        f"step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s)")
+    res = {}
+    for name, _ in kernels:
+        t = per[name]
+        avg = float(np.mean(t))
+        res[name] = {"algorithmic_bytes": nbytes[name], "us": round(avg * 1e3, 2),
+                     "us_min": round(min(t) * 1e3, 2), "us_max": round(max(t) * 1e3, 2),
+                     "GB/s": round(nbytes[name] / (avg * 1e6), 1),
+                     "frac_of_peak": round(nbytes[name] / (avg * 1e6) / HBM_PEAK_GBS, 4)}
+    log(f"fwd {res['fwd']['us']} us ({res['fwd']['GB/s']} GB/s), bwd {res['bwd']['us']} us "
+        f"({res['bwd']['GB/s']} GB/s), step {ms_per_step * 1e3:.1f} us ({value:.0f} GB/s)")
+
+    # each kernel alone, back to back: windows of launches between one pair of events
+    for name, fn in kernels:
+        ms = time_windows(lambda: fn(None))
+        res[name]["us_back_to_back"] = round(ms * 1e3, 2)
+        if probe:
+            mix = "fwd_like_2r1w" if name == "fwd" else "bwd_like_3r2w"
+            best = max(probe[m]["GB/s"] for m in probe if m.endswith(mix[-4:]))
+            res[name]["frac_of_best_ceiling"] = round(nbytes[name] / (ms * 1e6) / best, 4)
+        log(f"{name} back to back: {res[name]['us_back_to_back']} us")
 
     cold = None
     if args.cold_reps > 0:
-        (cfm, cfl), (cbm, cbl) = cold_ms["fwd"], cold_ms["bwd"]
-        cold = {"fwd_us": round(cfm * 1e3, 2), "fwd_us_min": round(cfl * 1e3, 2),
-                "fwd_GB/s": round(fwd_bytes / (cfm * 1e6), 1),
-                "bwd_us": round(cbm * 1e3, 2), "bwd_us_min": round(cbl * 1e3, 2),
-                "bwd_GB/s": round(bwd_bytes / (cbm * 1e6), 1),
-                "reps": args.cold_reps, "statistic": "median (GB/s from the median)"}
+        cold_ms = time_cold(kernels, args.cold_reps)
+        cold = {"reps": args.cold_reps, "statistic": "median (GB/s from the median)"}
+        for name in ("fwd", "bwd"):
+            med, low = cold_ms[name]
+            cold[f"{name}_us"] = round(med * 1e3, 2)
+            cold[f"{name}_us_min"] = round(low * 1e3, 2)
+            cold[f"{name}_GB/s"] = round(nbytes[name] / (med * 1e6), 1)
         log(f"cold: fwd {cold['fwd_GB/s']} GB/s, bwd {cold['bwd_GB/s']} GB/s")
-
-    probe = None
-    if not args.no_probe:
-        probe = {}
-        # same bytes per stream as the kernels: fwd = 2 reads of x/2 + 1 write; bwd = 3 + 2
-        nvec_elems = (rows * inter) // 8 * 8
-        bufs = [torch.empty(nvec_elems, dtype=torch.int16, device=dev) for _ in range(5)]
-        for b in bufs:
-            b.fill_(1)
-        for name, ns, nd in (("copy_1r1w", 1, 1), ("fwd_like_2r1w", 2, 1), ("bwd_like_3r2w", 3, 2)):
-            srcs, dsts = bufs[:ns], bufs[3:3 + nd]
-            ms = time_probe(srcs, dsts)
-            moved = (ns + nd) * nvec_elems * 2
-            probe[name] = {"bytes": moved, "us": round(ms * 1e3, 2),
-                           "GB/s": round(moved / (ms * 1e6), 1),
-                           "frac_of_peak": round(moved / (ms * 1e6) / HBM_PEAK_GBS, 4)}
-            log(f"probe {name}: {probe[name]['GB/s']} GB/s")
-        del bufs
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -502,13 +661,21 @@ def main() -> int:
             reps += 1
         cpu_step = spent / reps
         cpu = {"value": round((fwd_bytes + bwd_bytes) / (cpu_step * 1e9), 2), "unit": "GB/s",
-               "cores": threads, "kind": "oracle",
+               "cores": threads, "host_cores": oracle.host_cores(), "kind": "oracle",
                "sample": (f"the full {w.name} batch (fwd then bwd, {fwd_bytes + bwd_bytes} algorithmic "
-                          f"bytes) x {reps} reps, {spent:.1f} s total; {cpu_model()}"),
+                          f"bytes) x {reps} reps, {spent:.1f} s total, on {threads} threads "
+                          f"(OMP_NUM_THREADS caps the host's cores to this GPU's share); {cpu_model()}"),
                "ms_per_step": round(cpu_step * 1e3, 1)}
         log(f"cpu baseline: {cpu['value']} GB/s")
 
     traffic = measured_traffic(w.name)
+    trace = trace_average(w.name, "bwd")
+    roofline = {"bound": "hbm", "kernel": "swiglu_probs_bwd", "achieved": res["bwd"]["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["bwd"]["frac_of_peak"],
+                "traffic": traffic,
+                "timing": "each launch records its own start and end (hipExtLaunchKernel events)"}
+    if trace is not None:
+        roofline["trace_us"] = trace
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -517,24 +684,19 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "device_ms_per_step": round(dev_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "rows": rows, "inter": inter, "limit": L,
                    "n_used": inp["n_used"], "permutation_map": inp["permutation_map"] is not None,
                    "zero_padding": inp["zero_padding"], "io_dtype": "bf16", "probs_dtype": "f32",
-                   "seed": 0},
-        "fwd": {"algorithmic_bytes": fwd_bytes, "us": round(f_avg * 1e3, 2),
-                "us_min": round(min(fwd_ms) * 1e3, 2), "GB/s": round(f_gbs, 1),
-                "frac_of_peak": round(f_gbs / HBM_PEAK_GBS, 4)},
-        "bwd": {"algorithmic_bytes": bwd_bytes, "us": round(b_avg * 1e3, 2),
-                "us_min": round(min(bwd_ms) * 1e3, 2), "GB/s": round(b_gbs, 1),
-                "frac_of_peak": round(b_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "swiglu_probs_bwd_kernel",
-                     "achieved": round(b_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(b_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+                   "math": "fp32", "seed": 0},
+        "fwd": res["fwd"],
+        "bwd": res["bwd"],
+        "roofline": roofline,
         "cold": cold,
         "hbm_probe": probe,
         "cpu_baseline": cpu,

@@ -40,8 +40,12 @@
  *
  * Execution: work is enqueued on `stream` (0 = the null stream) and the call
  * returns without synchronising. No host read of device data, no allocation:
- * calls are hipGraph-capturable. The launch uses a fixed grid sized from the
- * device's compute-unit count (cached per device); the grid never changes the
+ * calls are hipGraph-capturable. The launch grid depends only on rows and inter
+ * (host sizes, never device data), as swiglu_probs_default_workgroups describes:
+ * one wave per row for rows of up to two column chunks, one workgroup per row for
+ * rows the four waves of a workgroup share, one workgroup per compute unit for
+ * rows of three chunks; never more than 16,777,215 workgroups, the waves then
+ * striding over the rows the grid does not cover. The grid never changes the
  * result bits. Calls are re-entrant and thread-safe.
  *
  * Errors: arguments are checked on the host before anything is launched; on any
@@ -133,16 +137,37 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
                                     const int32_t *n_used, const int32_t *permutation_map,
                                     int zero_padding, hipStream_t stream, int num_workgroups);
 
+/*
+ * The _ex calls with the kernel's own start and end recorded into `start` and `stop`
+ * (HIP events the caller created; either may be NULL) as part of the launch, with no
+ * separate event command on the stream (hipExtLaunchKernel). For benchmarks:
+ * hipEventElapsedTime(start, stop) is then the kernel's duration alone. The events
+ * must belong to the current device; otherwise as the _ex calls.
+ */
+swiglu_status_t swiglu_probs_fwd_timed(const uint16_t *x, const float *probs, uint16_t *y,
+                                       int64_t rows, int64_t inter, float limit,
+                                       const int32_t *n_used, const int32_t *permutation_map,
+                                       int zero_padding, hipStream_t stream, int num_workgroups,
+                                       hipEvent_t start, hipEvent_t stop);
+
+swiglu_status_t swiglu_probs_bwd_timed(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                       uint16_t *grad_x, float *grad_probs,
+                                       int64_t rows, int64_t inter, float limit,
+                                       const int32_t *n_used, const int32_t *permutation_map,
+                                       int zero_padding, hipStream_t stream, int num_workgroups,
+                                       hipEvent_t start, hipEvent_t stop);
+
 /* Workgroup count the library would launch for this call shape on the current
  * device (direction 0 = forward, 1 = backward), or -1 on error. Host only.
  * A row is cut into column chunks of U 16-byte vectors per lane (64 lanes): the
  * forward takes the U in 1..4 that leaves the fewest idle lanes (U = 2 for rows of
- * exactly 4 vectors per lane, read as two pipelined chunks), the backward cuts
- * rows of 4 or more vectors per lane into 4 or more chunks. Rows of one or two
- * chunks get one wave per row, ceil(rows / 4) workgroups; rows of three chunks one
- * workgroup per CU, balanced; rows of four or more one workgroup per row, its four
- * waves sharing the row. Never more than 16,777,215 workgroups (a dispatch holds
- * its work-item count in 32 bits); the waves then take several rows each. */
+ * exactly 4 vectors per lane), the backward cuts rows of 4 or more vectors per lane
+ * into 4 or more chunks. Rows of one or two chunks get one wave per row,
+ * ceil(rows / 4) workgroups (a forward row of at most 4 vectors per lane is then
+ * loaded whole); rows of three chunks one workgroup per CU, balanced; rows of four
+ * or more one workgroup per row, its four waves sharing the row. Never more than
+ * 16,777,215 workgroups (a dispatch holds its work-item count in 32 bits); the
+ * waves then take several rows each. */
 int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter);
 
 /* Static text for a status code. Never NULL. */

@@ -22,8 +22,12 @@ LIB_DIR = os.path.join(PKG, "_lib")
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
+# kernarg preload: the first 14 dwords of kernel arguments arrive in SGPRs when a wave
+# starts, so a kernel whose waves each handle one row issues its loads without first
+# waiting on the kernel-argument fetch (the kernels order their arguments for it).
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", f"-I{CSRC}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-Wall", "-Wno-unused-result"]
 
 LIBS = {

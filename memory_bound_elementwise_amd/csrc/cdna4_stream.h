@@ -33,12 +33,8 @@ constexpr int kRsrcWord3 = 0x00020000;
 // Cache-policy bits of streaming accesses (1 = sc0, 2 = nt, 16 = sc1). Nontemporal
 // loads and stores measured fastest in back-to-back runs on MI355X: plain stores
 // leave lines dirty in the 256 MB Infinity Cache for the next kernel to drain.
-#ifndef CDNA4_LOAD_AUX
-#define CDNA4_LOAD_AUX 2
-#endif
-#ifndef CDNA4_STORE_AUX
-#define CDNA4_STORE_AUX 2
-#endif
+constexpr int kLoadAux = 2;
+constexpr int kStoreAux = 2;
 
 // Every caller passes wave-uniform values (row addresses and lengths); readfirstlane
 // states that to the compiler, so the descriptor lives in SGPRs and no access needs a
@@ -70,12 +66,12 @@ __device__ __forceinline__ rsrc_t chunk_rsrc(const void *row, uint32_t bytes, ui
 
 __device__ __forceinline__ u32x4 load_vec(rsrc_t r, uint32_t voff)
 {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, CDNA4_LOAD_AUX);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadAux);
 }
 
 __device__ __forceinline__ void store_vec(rsrc_t r, u32x4 v, uint32_t voff)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, CDNA4_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kStoreAux);
 }
 
 // ---------------------------------------------------------------------------
@@ -106,23 +102,30 @@ __device__ __forceinline__ unsigned pack_f16x2(float lo, float hi)
 }
 
 // ---------------------------------------------------------------------------
-// Wave-wide sum with a fixed combination order; every lane ends with the total.
+// Wave-wide sum with a fixed combination order, returned as a wave-uniform value.
 // ---------------------------------------------------------------------------
-template <int kCtrl>
+// DPP move of v from the lane `kCtrl` selects; lanes of rows (16 lanes) outside
+// `kRowMask` get +0.
+template <int kCtrl, int kRowMask = 0xf>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, false));
 }
 
+// Pairs of lanes, then quads, halves of a row, rows: after the four in-row steps every
+// lane of a 16-lane row holds that row's total R_k. The two broadcasts then form
+// (R_3 + R_2) + (R_1 + R_0) in lane 63. fp32 addition is commutative, so every step
+// adds the same two values however its operands are ordered, and the order depends on
+// nothing but the lane.
 __device__ __forceinline__ float wave_sum(float v)
 {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lanes ^1
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lanes ^2
-    v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8
-    v += dpp<0x140>(v);  // row_mirror: the other half of each 16
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    return v;
+    v += dpp<0xB1>(v);        // quad_perm [1,0,3,2]: lanes ^1
+    v += dpp<0x4E>(v);        // quad_perm [2,3,0,1]: lanes ^2
+    v += dpp<0x141>(v);       // row_half_mirror: the other quad of each 8
+    v += dpp<0x140>(v);       // row_mirror: the other half of each 16
+    v += dpp<0x142, 0xa>(v);  // row_bcast:15: rows 1 and 3 add the total of rows 0 and 2
+    v += dpp<0x143, 0xc>(v);  // row_bcast:31: rows 2 and 3 add lane 31 (rows 0 + 1)
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -169,6 +172,38 @@ __device__ __forceinline__ void row_meta(int64_t ri, const RowSchedule &s, const
             p = probs[v];
         }
     }
+}
+
+// Bits of the `flags` argument of kernels that handle one row per wave or workgroup. The
+// flags say which optional row arguments exist, so a kernel reads those pointers (kernel
+// arguments past the preloaded ones) only when they are there.
+constexpr int kZeroPadding = 1;
+constexpr int kHasNUsed = 2;
+constexpr int kHasPerm = 4;
+
+// Slot of row `r` for a kernel that handles one row per wave or workgroup (r uniform):
+// -1 when the row is not live, i.e. at or past clamp(*n_used, 0, rows) or mapped outside
+// [0, rows). The loads are scalar; without n_used and map there are none.
+__device__ __forceinline__ int row_slot(int r, int rows, int flags, const int *__restrict__ n_used,
+                                        const int *__restrict__ perm)
+{
+    int live = rows;
+    if (flags & kHasNUsed) {
+        const int n = *n_used;
+        live = n < 0 ? 0 : (n > rows ? rows : n);
+    }
+    if (r >= live)
+        return -1;
+    const int v = (flags & kHasPerm) ? perm[r] : r;
+    return (unsigned)v < (unsigned)rows ? v : -1;
+}
+
+// probs[slot] for every lane (0 for slot < 0), through the vector memory path: a buffer
+// load of one dword at a wave-uniform address, issued like the row's streaming loads.
+__device__ __forceinline__ float load_row_prob(const float *__restrict__ probs, int slot)
+{
+    const rsrc_t r = make_rsrc(probs + (slot >= 0 ? slot : 0), slot >= 0 ? 4u : 0u);
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
 
 // Row sums. An Op with `kRowSum` true keeps a lane partial `acc` of a per-row sum; it
@@ -264,16 +299,42 @@ __device__ __forceinline__ void walk_rows(Op &op, const RowSchedule &sched, cons
     }
 }
 
+// The row total of a row whose four quarters the four waves of a workgroup hold as lane
+// partials `acc`: each wave writes its partials to part[w], and after one barrier wave 0
+// adds, lane by lane, the partials of waves 0, 1, 2, 3 in that order, then reduces the
+// 64 sums with wave_sum. The result is meaningful in wave 0 only. Every wave of the
+// workgroup must call it (it holds a barrier). The barrier is fenced on LDS alone:
+// only the partials cross it, and __syncthreads would also wait for every global
+// access in flight, the next item's prefetched loads included.
+__device__ __forceinline__ float row_sum_split(float (*part)[kWave], float acc, int w, int lane)
+{
+    part[w][lane] = acc;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    float t = 0.0f;
+    if (w == 0) {
+        t = part[0][lane];
+#pragma unroll
+        for (int i = 1; i < kWavesPerBlock; ++i)
+            t += part[i][lane];
+        t = wave_sum(t);
+    }
+    return t;
+}
+
 // A workgroup's walk over its rows (row r, r + G, r + 2G, ... for workgroup r of G), the
 // four waves sharing each row: wave w takes the column chunks
 // [floor(w nch / 4), floor((w + 1) nch / 4)), at least one each for nch >= 4. With
 // `spans` (uniform), the op has already given each wave its own quarter of the row and
 // nch counts the chunks of one quarter: every wave takes all nch of them. Per wave the
 // items (row, chunk) run through the same two-buffer pipeline as walk_rows. Row sums
-// (kRowSum ops) combine each wave's partial with wave_sum, then the four partials in
-// wave order through LDS, one barrier per row; the LDS pair alternates by row so a
-// fast wave cannot overwrite a partial that wave 0 has not read yet. Every wave of a
-// workgroup visits the same rows, so every barrier is reached by all four.
+// (kRowSum ops) go through LDS first: every wave writes its 64 lane partials, and after
+// one barrier per row wave 0 adds, lane by lane, the partials of waves 0, 1, 2, 3 in
+// that order and reduces the 64 results with wave_sum (row_sum_split above). The LDS
+// pair alternates by row so a fast wave cannot overwrite a partial that wave 0 has not
+// read yet. Every wave of a workgroup visits the same rows, so every barrier is reached
+// by all four.
 template <class Op>
 __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched, const int *__restrict__ perm,
                                                const float *__restrict__ probs, int nch,
@@ -285,7 +346,7 @@ __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched,
         walk_rows(op, sched, perm, probs, nch);
         return;
     }
-    __shared__ float partials[2][kWavesPerBlock];
+    __shared__ float partials[2][kWavesPerBlock][kWave];
     const int lane = lane_id();
     const int G = gridDim.x;
     const int w = wave_in_block();
@@ -325,22 +386,9 @@ __device__ __forceinline__ void walk_row_split(Op &op, const RowSchedule &sched,
             if constexpr (Op::kRowSum) {
                 // slot and the op's state are the same for all four waves: all or none sync
                 if (jj == nc - 1 && slot >= 0 && op.row_sum_wanted()) {
-                    const float part = wave_sum(op.acc);
-                    if (lane == 0)
-                        partials[parity][w] = part;
-                    // A barrier fenced on LDS alone: only the partials cross it, and
-                    // __syncthreads would also wait for every global access in flight,
-                    // the next item's prefetched loads included.
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                    __builtin_amdgcn_s_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                    if (w == 0) {
-                        float total = partials[parity][0];
-#pragma unroll
-                        for (int i = 1; i < kWavesPerBlock; ++i)
-                            total += partials[parity][i];
+                    const float total = row_sum_split(partials[parity], op.acc, w, lane);
+                    if (w == 0)
                         op.store_row_sum(slot, total);
-                    }
                     parity ^= 1;
                 }
             }
@@ -399,10 +447,7 @@ __device__ __forceinline__ void walk_blocks(Op &op, int64_t n_blocks)
 // MI355X's HBM3E more resident waves only add concurrent request streams: measured
 // throughput of the activation at the 1.1 GB shape falls from ~6.0 TB/s at one
 // workgroup per CU to ~5.6 TB/s at two to four.
-#ifndef CDNA4_BLOCKS_PER_CU
-#define CDNA4_BLOCKS_PER_CU 1
-#endif
-constexpr int kLaunchBlocksPerCU = CDNA4_BLOCKS_PER_CU;
+constexpr int kLaunchBlocksPerCU = 1;
 
 // Workgroups so that `units` (rows, blocks) split evenly over the waves: with at most
 // M waves, rounds = ceil(units / M) and waves = ceil(units / rounds). M is the CU count

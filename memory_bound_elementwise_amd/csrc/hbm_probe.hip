@@ -20,10 +20,7 @@ namespace {
 
 using namespace cdna4;
 
-#ifndef HBM_PROBE_U
-#define HBM_PROBE_U 4
-#endif
-constexpr int kU = HBM_PROBE_U;  // 16-byte vectors per lane per stream per block
+constexpr int kU = 4;  // 16-byte vectors per lane per stream per block
 constexpr uint32_t kBlockBytes = kU * kWave * kVecBytes;  // 4 KiB per stream per block at kU = 4
 
 struct Ptrs {

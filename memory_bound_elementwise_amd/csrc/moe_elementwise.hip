@@ -686,8 +686,8 @@ __global__ __launch_bounds__(kBlock) void unpermute_pipelined_kernel(const uint1
             for (int u = 0; u < U; ++u) {
                 if constexpr (kSplit) {
                     const uint32_t o = (uint32_t)u * kWave * kVecBytes + (uint32_t)lane * 8u;
-                    const auto lo = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, CDNA4_LOAD_AUX);
-                    const auto hi = __builtin_amdgcn_raw_buffer_load_b64(rs, o + kWave * 8u, 0, CDNA4_LOAD_AUX);
+                    const auto lo = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, kLoadAux);
+                    const auto hi = __builtin_amdgcn_raw_buffer_load_b64(rs, o + kWave * 8u, 0, kLoadAux);
                     b.v[g][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 } else {
                     b.v[g][u] = load_vec(rs, (uint32_t)(lane + u * kWave) * kVecBytes);
@@ -868,11 +868,6 @@ int64_t row_chunks(int64_t octs, int U) { return (octs + (int64_t)U * kWave - 1)
 //     faster than the split. The forward, with no barrier, stays on the split (quarters
 //     measured 0.3-1% slower).
 //   * Shorter rows go one per wave (walk_row_split falls back to walk_rows).
-// MOE_ROUTER_SPANS = 0 turns the quarters off, 1 takes them in both directions whenever
-// the row splits into quarters of whole octs.
-#ifndef MOE_ROUTER_SPANS
-#define MOE_ROUTER_SPANS -1
-#endif
 
 struct RouterPlan {
     int U;
@@ -885,13 +880,12 @@ RouterPlan plan_router(int64_t tokens, int64_t hidden, int cus, int num_workgrou
     const int64_t octs = hidden / 8;
     RouterPlan pl{pick_u(octs), 0, 0};
     const int64_t nch = row_chunks(octs, pl.U);
-    if (octs % kWavesPerBlock == 0 && nch >= kWavesPerBlock &&
-        (MOE_ROUTER_SPANS == 1 || (MOE_ROUTER_SPANS != 0 && backward))) {
+    if (backward && octs % kWavesPerBlock == 0 && nch >= kWavesPerBlock) {
         const int64_t q = octs / kWavesPerBlock;
         const int Uq = pick_u(q);
         const int64_t span_slots = row_chunks(q, Uq) * Uq;                      // per lane
         const int64_t split_slots = (nch + kWavesPerBlock - 1) / kWavesPerBlock * pl.U;
-        if (MOE_ROUTER_SPANS == 1 || (nch % kWavesPerBlock != 0 && span_slots <= split_slots)) {
+        if (nch % kWavesPerBlock != 0 && span_slots <= split_slots) {
             pl.U = Uq;
             pl.spans = 1;
         }
@@ -911,10 +905,7 @@ moe_status_t launched()
 // residual add: octs per lane per block (U) of the flat walk. U = 2 moves 2 KiB per wave
 // per stream (bf16), the block the plain streaming probe moves fastest on MI355X; at
 // 6720 x 7168 bf16 it measured 61.3 against 61.7 us for 4 KiB blocks, interleaved.
-#ifndef MOE_RESIDUAL_U
-#define MOE_RESIDUAL_U 2
-#endif
-constexpr int kResidualU = MOE_RESIDUAL_U;
+constexpr int kResidualU = 2;
 
 template <int DT>
 void launch_residual(int blocks, hipStream_t st, const void *e, const void *s, const void *r, void *o,
@@ -1010,37 +1001,16 @@ void launch_sqrelu_bwd(int U, int blocks, hipStream_t st, const uint16_t *x, con
 }
 
 // unpermute: G experts per batch of loads, U octs per lane per chunk
-#ifndef MOE_UNPERMUTE_U
-#define MOE_UNPERMUTE_U 4
-#endif
-#ifndef MOE_UNPERMUTE_G
-#define MOE_UNPERMUTE_G 4
-#endif
-#ifndef MOE_UNPERMUTE_BPC
-#define MOE_UNPERMUTE_BPC 2
-#endif
-#ifndef MOE_SQRELU_CLAMP_MAX_U
-#define MOE_SQRELU_CLAMP_MAX_U 2
-#endif
-#ifndef MOE_UNPERMUTE_PIPE_U
-#define MOE_UNPERMUTE_PIPE_U 2
-#endif
-#ifndef MOE_UNPERMUTE_PIPE_BPC
-#define MOE_UNPERMUTE_PIPE_BPC 1
-#endif
-#ifndef MOE_UNPERMUTE_PIPELINED
-#define MOE_UNPERMUTE_PIPELINED 1
-#endif
-constexpr int kUnpermuteU = MOE_UNPERMUTE_U;
-constexpr int kUnpermuteG = MOE_UNPERMUTE_G;
+constexpr int kUnpermuteU = 4;
+constexpr int kUnpermuteG = 4;
 // The unpermute waits on each group of gathers before adding it, so it keeps more
 // waves resident than the pure streams do.
-constexpr int kUnpermuteBlocksPerCU = MOE_UNPERMUTE_BPC;
+constexpr int kUnpermuteBlocksPerCU = 2;
 // Up to this many local experts take the pipelined unpermute, one workgroup per CU
 // (measured best: 110 us against 113 us at two, for 6720 tokens x 8 experts).
-constexpr int kUnpermutePipelinedMaxExperts = MOE_UNPERMUTE_PIPELINED ? 8 : 0;
-constexpr int kUnpermutePipeU = MOE_UNPERMUTE_PIPE_U;
-constexpr int kUnpermutePipeBlocksPerCU = MOE_UNPERMUTE_PIPE_BPC;
+constexpr int kUnpermutePipelinedMaxExperts = 8;
+constexpr int kUnpermutePipeU = 2;
+constexpr int kUnpermutePipeBlocksPerCU = 1;
 // The soft-clamped squared ReLU (forward ~19, backward ~30 vector instructions per
 // element) keeps the VALU 73% / 86% busy. It runs with 2 octs per lane per chunk
 // (83 registers, up to 6 waves per SIMD) and one wave per row whatever the row length.
@@ -1048,7 +1018,7 @@ constexpr int kUnpermutePipeBlocksPerCU = MOE_UNPERMUTE_PIPE_BPC;
 // unclamped kernels, against 81.9 / 118.9 us with a balanced grid of 1920
 // resident-sized workgroups, whose last dispatch round ran half empty. Without the
 // clamp the kernel is a plain stream and follows the default grid rule.
-constexpr int kSquaredReluClampMaxU = MOE_SQRELU_CLAMP_MAX_U;
+constexpr int kSquaredReluClampMaxU = 2;
 
 // An explicit workgroup count: 0 (the default grid) up to the dispatch limit.
 bool bad_grid(int num_workgroups) { return num_workgroups < 0 || num_workgroups > kMaxWorkgroups; }

@@ -13,39 +13,34 @@
 // Design (HBM-bound; no MFMA):
 //   * Lane l of a wave handles the 16-byte vectors l, l+64, l+128, ... of the gate
 //     half, the up half and (backward) grad_y: every access is 128 bits wide and one
-//     wave instruction covers 1 KiB of contiguous memory. A row is processed in
-//     chunks of U vectors per lane: the forward takes the U that leaves the fewest
-//     idle lanes (two chunks of 2 for rows of exactly 4 vectors per lane), the backward
-//     cuts rows of 4 or more vectors per lane into 4 or more chunks. Rows of 4 or more chunks are shared by a workgroup's four waves, a
-//     quarter of the chunks each (walk_row_split); shorter rows go one per wave
-//     (walk_rows).
+//     wave instruction covers 1 KiB of contiguous memory.
 //   * Every load and store is a buffer instruction on a per-row buffer resource
 //     whose size is the row's byte length, or 0 for a row that is not live. The
 //     hardware range check then does all masking: lanes past the row end and rows
 //     that are not live read zeros without touching memory, and their stores are
 //     dropped (or, for zero-padded rows, write the +0 that zero inputs produce).
-//     No branch guards a memory instruction, so the compiler's wait counts stay
-//     exact across the software pipeline below.
-//   * Software pipeline: each wave holds two register buffers and issues the loads
-//     of its next chunk (usually its next row) before computing the current one,
-//     so its own memory traffic overlaps its arithmetic.
-//   * Waves (or workgroups, for shared rows) stride over rows with a fixed grid
-//     (row r, r + W, r + 2W, ...), so the launch never depends on device data and
-//     is graph-safe. By default the grid has one wave (or workgroup) per row, up to
-//     the dispatch limit of 16,777,215 workgroups; rows of exactly three chunks get
-//     one persistent workgroup per CU instead, sized so every wave gets the same
-//     number of rows (walk_workgroups in cdna4_stream.h).
-//   * Per-row metadata (permutation slot and probability) for a wave's next 64
-//     rows is gathered with one vector load, one row per lane, and broadcast with
-//     v_readlane when the row is processed: no per-row dependent scalar loads.
-//   * The probability gradient: each lane sums its own columns in a fixed order,
-//     then a butterfly over the wave (DPP quad/row permutes, then two lane
-//     exchanges) combines the 64 partials; on shared rows the four waves' totals
-//     are then added in wave order through LDS. The order depends only on the row
-//     width, never on the grid, so the bits are grid-invariant.
+//     No branch guards a memory instruction, so the compiler's wait counts are exact.
+//   * Default launches are straight-line kernels with one unit of work per wave:
+//     the forward gives each wave one whole row (up to 4 vectors per lane per stream,
+//     all loads issued at once); the backward gives each wave one whole row of up to
+//     3 vectors per lane, and splits rows of exactly 4 chunks among the four waves of
+//     a workgroup, one chunk each (the 2,048- and 4,096-column rows). The row's slot
+//     and probability come from scalar loads, so a wave carries no per-row bookkeeping
+//     beyond its own row.
+//   * Other shapes, and launches with an explicit workgroup count, run the fixed-grid
+//     walks of cdna4_stream.h: waves (or workgroups, for shared rows) stride over
+//     rows (row r, r + W, r + 2W, ...), each wave pipelining the loads of its next
+//     chunk ahead of the current one's arithmetic. The launch never depends on device
+//     data and is graph-safe; both forms give the same bits, because the element
+//     arithmetic, each lane's column order and the reduction order are the same.
+//   * The probability gradient: each lane sums its own columns in a fixed order, then
+//     a fixed DPP butterfly over the wave combines the 64 partials; on shared rows the
+//     four waves first add their lane partials in wave order through LDS. The order
+//     depends only on the row width, never on the grid, so the bits are grid-invariant.
 //   * fp32 -> bf16 uses v_cvt_pk_bf16_f32 (round to nearest even, two values per
 //     instruction); the clamps use v_minimum3/v_maximum3 (NaN-propagating, as
 //     torch.clamp); the inclusive masks are "the clamp left the value unchanged".
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -60,13 +55,7 @@ namespace {
 
 using namespace cdna4;
 
-#ifndef SWIGLU_MAX_U
-#define SWIGLU_MAX_U 4
-#endif
-constexpr int kMaxU = SWIGLU_MAX_U;  // 16-byte vectors per lane per stream per chunk
-#ifndef SWIGLU_WALK
-#define SWIGLU_WALK walk_row_split
-#endif
+constexpr int kMaxU = 4;  // 16-byte vectors per lane per stream per chunk
 constexpr float kNegLog2e = -1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -82,42 +71,81 @@ __device__ __forceinline__ float clamp_up(float b, float L)
     return __builtin_elementwise_maximum(__builtin_elementwise_minimum(b, L), -L);
 }
 
-// logistic sigmoid 1 / (1 + e^-z) from v_exp_f32 (2^x) and v_rcp_f32.
+// logistic sigmoid sig = 1 / (1 + e^-z) and 1 - sig, from v_exp_f32 (2^x) and v_rcp_f32.
 // v_rcp_f32 flushes subnormal results to zero, and 1 / (1 + e^-z) is subnormal once
 // 1 + e^-z exceeds 2^126 (z < -87.3), where silu(z) = z * sigmoid(z) is still a normal
 // number. The reciprocal is therefore taken of 2^-64 * (1 + e^-z) (one fma, exact: a
 // power-of-two scale of a value >= 1), which keeps it normal, and the result is scaled
 // back by 2^-64 in a multiply, which does produce subnormals. For e^-z = inf (z < -88.7)
-// the sigmoid is 0, as 1 / (1 + inf) is in fp32.
-__device__ __forceinline__ float sigmoid(float z)
+// the sigmoid is 0, as 1 / (1 + inf) is in fp32. 1 - sig is one fma of the scaled
+// reciprocal.
+__device__ __forceinline__ void sigmoid(float z, float &sig, float &one_minus_sig)
 {
     constexpr float kTwoM64 = 0x1p-64f;
-    float e = __builtin_amdgcn_exp2f(z * kNegLog2e);
-    return __builtin_amdgcn_rcpf(__builtin_fmaf(e, kTwoM64, kTwoM64)) * kTwoM64;
+    const float e = __builtin_amdgcn_exp2f(z * kNegLog2e);
+    const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(e, kTwoM64, kTwoM64));  // 2^64 sig
+    sig = r * kTwoM64;
+    one_minus_sig = __builtin_fmaf(r, -kTwoM64, 1.0f);
 }
 
 __device__ __forceinline__ float fwd_elem(float a, float b, float p, float L)
 {
     float cg = clamp_gate(a, L);
     float cu = clamp_up(b, L);
-    float s = cg * sigmoid(cg);
+    float sig, oms;
+    sigmoid(cg, sig, oms);
+    float s = cg * sig;
     return (s * cu) * p;
 }
 
-// Autograd chain of y = (silu(cg) * cu) * p with inclusive clamp masks.
+// Autograd chain of y = (silu(cg) * cu) * p with inclusive clamp masks. The silu
+// derivative sig * (1 + cg * (1 - sig)) is taken as sig + s * (1 - sig), one fma: the
+// same value (s = cg * sig), one rounding instead of two. Near silu's minimum
+// (cg = -1.2785, where the derivative crosses 0) both forms cancel alike; a bf16 gate
+// stays at least 0.0027 away from it, and over every bf16 gate the relative error of
+// either form in fp32 stays under 1e-5 (an fp64 check), far inside half a bf16 ulp.
 __device__ __forceinline__ void bwd_elem(float a, float b, float g, float p, float L,
                                          float &dg, float &du, float &acc)
 {
     float cg = clamp_gate(a, L);
     float cu = clamp_up(b, L);
-    float sig = sigmoid(cg);
+    float sig, oms;
+    sigmoid(cg, sig, oms);
     float s = cg * sig;
     float gp = g * p;
-    float dsilu = sig * (1.0f + cg * (1.0f - sig));
+    float dsilu = __builtin_fmaf(s, oms, sig);
     // a <= L  <=>  min(a, L) == a ;  -L <= b <= L  <=>  clamp(b) == b  (false for NaN)
     dg = (cg == a) ? (gp * cu) * dsilu : 0.0f;
     du = (cu == b) ? gp * s : 0.0f;
     acc += g * (s * cu);
+}
+
+// Eight elements of a 16-byte vector (four packed bf16 pairs): forward.
+__device__ __forceinline__ u32x4 fwd_vec(const u32x4 &g, const u32x4 &u, float p, float L)
+{
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float y0 = fwd_elem(bf16_lo(g[q]), bf16_lo(u[q]), p, L);
+        const float y1 = fwd_elem(bf16_hi(g[q]), bf16_hi(u[q]), p, L);
+        o[q] = pack_bf16x2(y0, y1);
+    }
+    return o;
+}
+
+// Eight elements of a 16-byte vector: backward, in column order (lo then hi of each
+// pair), adding to the lane's row-sum partial in that order.
+__device__ __forceinline__ void bwd_vec(const u32x4 &g, const u32x4 &u, const u32x4 &d, float p, float L,
+                                        u32x4 &og, u32x4 &ou, float &acc)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float dg0, du0, dg1, du1;
+        bwd_elem(bf16_lo(g[q]), bf16_lo(u[q]), bf16_lo(d[q]), p, L, dg0, du0, acc);
+        bwd_elem(bf16_hi(g[q]), bf16_hi(u[q]), bf16_hi(d[q]), p, L, dg1, du1, acc);
+        og[q] = pack_bf16x2(dg0, dg1);
+        ou[q] = pack_bf16x2(du0, du1);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -154,30 +182,22 @@ struct FwdOp {
         const uint32_t n = (slot >= 0 || zero_padding) ? (uint32_t)inter * 2u : 0u;
         const rsrc_t ry = chunk_rsrc(y + r * inter, n, (uint32_t)c * U * kWave * kVecBytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float y0 = fwd_elem(bf16_lo(b.g[u][q]), bf16_lo(b.u[u][q]), p, L);
-                float y1 = fwd_elem(bf16_hi(b.g[u][q]), bf16_hi(b.u[u][q]), p, L);
-                o[q] = pack_bf16x2(y0, y1);
-            }
-            store_vec(ry, o, voff + u * kWave * kVecBytes);
-        }
+        for (int u = 0; u < U; ++u)
+            store_vec(ry, fwd_vec(b.g[u], b.u[u], p, L), voff + u * kWave * kVecBytes);
     }
 };
 
 template <int U>
 __global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ probs, uint16_t *__restrict__ y,
-    int rows, int inter, float L, const int *__restrict__ n_used, const int *__restrict__ perm,
+    const int *__restrict__ n_used, const int *__restrict__ perm, int rows, int inter, float L,
     int zero_padding)
 {
     const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
     const int vpr = inter / 8;
     const int nch = (vpr + U * kWave - 1) / (U * kWave);
     FwdOp<U> op{x, y, inter, L, zero_padding, (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes};
-    SWIGLU_WALK(op, sched, perm, probs, nch);
+    walk_row_split(op, sched, perm, probs, nch);
 }
 
 // ---------------------------------------------------------------------------
@@ -223,14 +243,7 @@ struct BwdOp {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             u32x4 og, ou;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float dg0, du0, dg1, du1;
-                bwd_elem(bf16_lo(b.g[u][q]), bf16_lo(b.u[u][q]), bf16_lo(b.d[u][q]), p, L, dg0, du0, acc);
-                bwd_elem(bf16_hi(b.g[u][q]), bf16_hi(b.u[u][q]), bf16_hi(b.d[u][q]), p, L, dg1, du1, acc);
-                og[q] = pack_bf16x2(dg0, dg1);
-                ou[q] = pack_bf16x2(du0, du1);
-            }
+            bwd_vec(b.g[u], b.u[u], b.d[u], p, L, og, ou, acc);
             store_vec(rdg, og, voff + u * kWave * kVecBytes);
             store_vec(rdu, ou, voff + u * kWave * kVecBytes);
         }
@@ -246,16 +259,147 @@ struct BwdOp {
 
 template <int U>
 __global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_kernel(
-    const uint16_t *__restrict__ x, const float *__restrict__ probs, const uint16_t *__restrict__ gy,
-    uint16_t *__restrict__ gx, float *__restrict__ gprobs, int rows, int inter, float L,
-    const int *__restrict__ n_used, const int *__restrict__ perm, int zero_padding)
+    int rows, int inter, float L, int zero_padding, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ gy, uint16_t *__restrict__ gx, const int *__restrict__ n_used,
+    const int *__restrict__ perm, const float *__restrict__ probs, float *__restrict__ gprobs)
 {
     const RowSchedule sched = make_schedule(rows, n_used, zero_padding);
     const int vpr = inter / 8;
     const int nch = (vpr + U * kWave - 1) / (U * kWave);
     BwdOp<U> op{x, gy, gx, gprobs, inter, L, zero_padding,
                 (uint32_t)(threadIdx.x & (kWave - 1)) * kVecBytes, 0.0f};
-    SWIGLU_WALK(op, sched, perm, probs, nch);
+    walk_row_split(op, sched, perm, probs, nch);
+}
+
+// ---------------------------------------------------------------------------
+// Straight-line kernels of the default launches: one unit of work per wave
+// ---------------------------------------------------------------------------
+// Forward, one wave per row (row = the wave's index in the grid), every vector of the
+// row at once: V = ceil(inter / 512) <= 4 vectors per lane per stream.
+template <int V>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_fwd_row_kernel(
+    int rows, int inter, float L, int flags, const uint16_t *__restrict__ x,
+    const float *__restrict__ probs, uint16_t *__restrict__ y, const int *__restrict__ n_used,
+    const int *__restrict__ perm)
+{
+    const int r = wave_id();
+    if (r >= rows)
+        return;
+    const int slot = row_slot(r, rows, flags, n_used, perm);
+    if (slot < 0 && !(flags & kZeroPadding))
+        return;
+    const uint32_t row_bytes = (uint32_t)inter * 2u;
+    const uint32_t n_in = slot >= 0 ? row_bytes : 0u;
+    const uint16_t *gate = x + (int64_t)r * 2 * inter;
+    const rsrc_t rg = make_rsrc(gate, n_in), ru = make_rsrc(gate + inter, n_in);
+    const uint32_t voff = (uint32_t)lane_id() * kVecBytes;
+    const float p = load_row_prob(probs, slot);
+    u32x4 g[V], u[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        g[v] = load_vec(rg, voff + v * kWave * kVecBytes);
+        u[v] = load_vec(ru, voff + v * kWave * kVecBytes);
+    }
+    const rsrc_t ry = make_rsrc(y + (int64_t)r * inter, row_bytes);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+        store_vec(ry, fwd_vec(g[v], u[v], p, L), voff + v * kWave * kVecBytes);
+}
+
+// Backward, one wave per row, every vector of the row at once (V <= 3 vectors per lane
+// per stream: rows of one chunk). The row sum is the lane partials in column order,
+// then wave_sum: walk_rows' order for a one-chunk row.
+template <int V>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_row_kernel(
+    int rows, int inter, float L, int flags, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ gy, uint16_t *__restrict__ gx, const float *__restrict__ probs,
+    float *__restrict__ gprobs, const int *__restrict__ n_used, const int *__restrict__ perm)
+{
+    const int r = wave_id();
+    if (r >= rows)
+        return;
+    const int slot = row_slot(r, rows, flags, n_used, perm);
+    if (slot < 0 && !(flags & kZeroPadding))
+        return;
+    const uint32_t row_bytes = (uint32_t)inter * 2u;
+    const uint32_t n_in = slot >= 0 ? row_bytes : 0u;
+    const uint16_t *gate = x + (int64_t)r * 2 * inter;
+    const rsrc_t rg = make_rsrc(gate, n_in), ru = make_rsrc(gate + inter, n_in);
+    const rsrc_t rd = make_rsrc(gy + (int64_t)r * inter, n_in);
+    const uint32_t voff = (uint32_t)lane_id() * kVecBytes;
+    const float p = load_row_prob(probs, slot);
+    u32x4 g[V], u[V], d[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        g[v] = load_vec(rg, voff + v * kWave * kVecBytes);
+        u[v] = load_vec(ru, voff + v * kWave * kVecBytes);
+        d[v] = load_vec(rd, voff + v * kWave * kVecBytes);
+    }
+    uint16_t *dgate = gx + (int64_t)r * 2 * inter;
+    const rsrc_t rdg = make_rsrc(dgate, row_bytes), rdu = make_rsrc(dgate + inter, row_bytes);
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        u32x4 og, ou;
+        bwd_vec(g[v], u[v], d[v], p, L, og, ou, acc);
+        store_vec(rdg, og, voff + v * kWave * kVecBytes);
+        store_vec(rdu, ou, voff + v * kWave * kVecBytes);
+    }
+    if (slot >= 0 && gprobs) {
+        const float total = wave_sum(acc);
+        if (lane_id() == 0)
+            gprobs[slot] = total;
+    }
+}
+
+// Backward, one workgroup per row (row = workgroup index) cut into exactly four chunks
+// of U vectors per lane, wave w taking chunk w. The row sum goes through row_sum_split:
+// walk_row_split's order for a row of four chunks.
+template <int U>
+__global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_quarter_kernel(
+    int rows, int inter, float L, int flags, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ gy, uint16_t *__restrict__ gx, const float *__restrict__ probs,
+    float *__restrict__ gprobs, const int *__restrict__ n_used, const int *__restrict__ perm)
+{
+    __shared__ float part[kWavesPerBlock][kWave];
+    const int r = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+    const int w = wave_in_block();
+    if (r >= rows)
+        return;
+    // the same for all four waves: either all return here or all reach the barrier below
+    const int slot = row_slot(r, rows, flags, n_used, perm);
+    if (slot < 0 && !(flags & kZeroPadding))
+        return;
+    const uint32_t row_bytes = (uint32_t)inter * 2u;
+    const uint32_t n_in = slot >= 0 ? row_bytes : 0u;
+    const uint32_t off = (uint32_t)w * U * kWave * kVecBytes;
+    const uint16_t *gate = x + (int64_t)r * 2 * inter;
+    const rsrc_t rg = chunk_rsrc(gate, n_in, off), ru = chunk_rsrc(gate + inter, n_in, off);
+    const rsrc_t rd = chunk_rsrc(gy + (int64_t)r * inter, n_in, off);
+    const uint32_t voff = (uint32_t)lane_id() * kVecBytes;
+    const float p = load_row_prob(probs, slot);
+    u32x4 g[U], u[U], d[U];
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+        g[v] = load_vec(rg, voff + v * kWave * kVecBytes);
+        u[v] = load_vec(ru, voff + v * kWave * kVecBytes);
+        d[v] = load_vec(rd, voff + v * kWave * kVecBytes);
+    }
+    uint16_t *dgate = gx + (int64_t)r * 2 * inter;
+    const rsrc_t rdg = chunk_rsrc(dgate, row_bytes, off), rdu = chunk_rsrc(dgate + inter, row_bytes, off);
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+        u32x4 og, ou;
+        bwd_vec(g[v], u[v], d[v], p, L, og, ou, acc);
+        store_vec(rdg, og, voff + v * kWave * kVecBytes);
+        store_vec(rdu, ou, voff + v * kWave * kVecBytes);
+    }
+    if (slot >= 0 && gprobs) {
+        const float total = row_sum_split(part, acc, w, lane_id());
+        if (w == 0 && lane_id() == 0)
+            gprobs[slot] = total;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -358,6 +502,33 @@ int pick_u_fwd(int64_t vpr)
     return u == 4 && kMaxU >= 2 ? 2 : pick_u(vpr);
 }
 
+// Default launches take the straight-line kernels where one unit of work per wave
+// fits: the forward for rows of at most 4 vectors per lane per stream (inter <= 2048,
+// one wave per row), the backward for rows of at most 3 (inter <= 1536, one wave per
+// row) and for rows that pick_u_bwd cuts into exactly four chunks (one per wave of a
+// workgroup: 2,048 and 4,096 columns among others). Their grids are the walks' default
+// grids for those shapes. Where one unit per wave would need more than 16,777,215
+// workgroups the walks take over, with the same bits. Each returns the kernel's vector
+// count (V, or U for the quarters), 0 when the shape takes a walk.
+int lean_fwd_vectors(int64_t rows, int64_t vpr)
+{
+    const int64_t u = (vpr + kWave - 1) / kWave;
+    return u <= 4 && (rows + kWavesPerBlock - 1) / kWavesPerBlock <= kMaxWorkgroups ? (int)u : 0;
+}
+
+int lean_bwd_row_vectors(int64_t rows, int64_t vpr)
+{
+    const int64_t u = (vpr + kWave - 1) / kWave;
+    return u <= 3 && (rows + kWavesPerBlock - 1) / kWavesPerBlock <= kMaxWorkgroups ? (int)u : 0;
+}
+
+int lean_bwd_quarter_u(int64_t rows, int64_t vpr)
+{
+    const int64_t u = (vpr + kWave - 1) / kWave;
+    const int U = pick_u_bwd(vpr);
+    return u >= kWavesPerBlock && chunks_per_row(vpr, U) == kWavesPerBlock && rows <= kMaxWorkgroups ? U : 0;
+}
+
 // Address ranges, for the check that no output overlaps an input.
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -402,34 +573,108 @@ swiglu_status_t fail_hip(hipError_t e)
     return SWIGLU_ERR_HIP;
 }
 
+// Every launch goes through hipExtLaunchKernel: with events (the timed entry points) the
+// kernel's own start and end are recorded into them, with no separate command on the
+// stream; with null events it is a plain launch.
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start, stop;
+};
+
 template <int U>
-void launch_fwd(int blocks, hipStream_t stream, const uint16_t *x, const float *probs, uint16_t *y,
+void launch_fwd(const Launch &l, int blocks, const uint16_t *x, const float *probs, uint16_t *y,
                 int rows, int inter, float limit, const int32_t *n_used, const int32_t *perm, int zp)
 {
-    hipLaunchKernelGGL(swiglu_probs_fwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream, x, probs, y,
-                       rows, inter, limit, n_used, perm, zp);
+    hipExtLaunchKernelGGL(swiglu_probs_fwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, l.stream, l.start, l.stop, 0,
+                          x, probs, y, n_used, perm, rows, inter, limit, zp);
 }
 
 template <int U>
-void launch_bwd(int blocks, hipStream_t stream, const uint16_t *x, const float *probs,
+void launch_bwd(const Launch &l, int blocks, const uint16_t *x, const float *probs,
                 const uint16_t *gy, uint16_t *gx, float *gp, int rows, int inter, float limit,
                 const int32_t *n_used, const int32_t *perm, int zp)
 {
-    hipLaunchKernelGGL(swiglu_probs_bwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, stream, x, probs, gy,
-                       gx, gp, rows, inter, limit, n_used, perm, zp);
+    hipExtLaunchKernelGGL(swiglu_probs_bwd_kernel<U>, dim3(blocks), dim3(kBlock), 0, l.stream, l.start, l.stop, 0,
+                          rows, inter, limit, zp, x, gy, gx, n_used, perm, probs, gp);
 }
 
-}  // namespace
+// The flags argument of the one-row-per-wave kernels.
+int row_flags(int zp, const int32_t *n_used, const int32_t *perm)
+{
+    return (zp ? kZeroPadding : 0) | (n_used ? kHasNUsed : 0) | (perm ? kHasPerm : 0);
+}
 
-// ---------------------------------------------------------------------------
-// C ABI
-// ---------------------------------------------------------------------------
-extern "C" {
+template <int V>
+void launch_fwd_row_v(const Launch &l, const uint16_t *x, const float *probs, uint16_t *y, int rows,
+                      int inter, float limit, const int32_t *n_used, const int32_t *perm, int zp)
+{
+    const int blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipExtLaunchKernelGGL(swiglu_probs_fwd_row_kernel<V>, dim3(blocks), dim3(kBlock), 0, l.stream, l.start, l.stop,
+                          0, rows, inter, limit, row_flags(zp, n_used, perm), x, probs, y, n_used, perm);
+}
 
-swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint16_t *y,
-                                    int64_t rows, int64_t inter, float limit,
-                                    const int32_t *n_used, const int32_t *permutation_map,
-                                    int zero_padding, hipStream_t stream, int num_workgroups)
+// The straight-line forward of a default launch; false (nothing launched) when the
+// shape takes a walk.
+bool launch_fwd_row(const Launch &l, const uint16_t *x, const float *probs, uint16_t *y, int64_t rows,
+                    int64_t inter, float limit, const int32_t *n_used, const int32_t *perm, int zp)
+{
+    const int r = (int)rows, n = (int)inter;
+    switch (lean_fwd_vectors(rows, inter / 8)) {
+    case 1: launch_fwd_row_v<1>(l, x, probs, y, r, n, limit, n_used, perm, zp); return true;
+    case 2: launch_fwd_row_v<2>(l, x, probs, y, r, n, limit, n_used, perm, zp); return true;
+    case 3: launch_fwd_row_v<3>(l, x, probs, y, r, n, limit, n_used, perm, zp); return true;
+    case 4: launch_fwd_row_v<4>(l, x, probs, y, r, n, limit, n_used, perm, zp); return true;
+    default: return false;
+    }
+}
+
+template <int V>
+void launch_bwd_row_v(const Launch &l, const uint16_t *x, const float *probs, const uint16_t *gy,
+                      uint16_t *gx, float *gp, int rows, int inter, float limit, const int32_t *n_used,
+                      const int32_t *perm, int zp)
+{
+    const int blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipExtLaunchKernelGGL(swiglu_probs_bwd_row_kernel<V>, dim3(blocks), dim3(kBlock), 0, l.stream, l.start, l.stop,
+                          0, rows, inter, limit, row_flags(zp, n_used, perm), x, gy, gx, probs, gp, n_used, perm);
+}
+
+template <int U>
+void launch_bwd_quarter_u(const Launch &l, const uint16_t *x, const float *probs, const uint16_t *gy,
+                          uint16_t *gx, float *gp, int rows, int inter, float limit, const int32_t *n_used,
+                          const int32_t *perm, int zp)
+{
+    hipExtLaunchKernelGGL(swiglu_probs_bwd_quarter_kernel<U>, dim3(rows), dim3(kBlock), 0, l.stream, l.start,
+                          l.stop, 0, rows, inter, limit, row_flags(zp, n_used, perm), x, gy, gx, probs, gp, n_used,
+                          perm);
+}
+
+// The straight-line backward of a default launch; false (nothing launched) when the
+// shape takes a walk.
+bool launch_bwd_lean(const Launch &l, const uint16_t *x, const float *probs, const uint16_t *gy,
+                     uint16_t *gx, float *gp, int64_t rows, int64_t inter, float limit,
+                     const int32_t *n_used, const int32_t *perm, int zp)
+{
+    const int r = (int)rows, n = (int)inter;
+    switch (lean_bwd_row_vectors(rows, inter / 8)) {
+    case 1: launch_bwd_row_v<1>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    case 2: launch_bwd_row_v<2>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    case 3: launch_bwd_row_v<3>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    default: break;
+    }
+    switch (lean_bwd_quarter_u(rows, inter / 8)) {
+    case 1: launch_bwd_quarter_u<1>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    case 2: launch_bwd_quarter_u<2>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    case 3: launch_bwd_quarter_u<3>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    case 4: launch_bwd_quarter_u<4>(l, x, probs, gy, gx, gp, r, n, limit, n_used, perm, zp); return true;
+    default: return false;
+    }
+}
+
+// Validation, then the launch. Arguments are checked on the host before anything is
+// launched; on any error nothing is written.
+swiglu_status_t fwd_impl(const uint16_t *x, const float *probs, uint16_t *y, int64_t rows, int64_t inter,
+                         float limit, const int32_t *n_used, const int32_t *permutation_map, int zero_padding,
+                         int num_workgroups, const Launch &l)
 {
     swiglu_status_t st = check_shape(rows, inter, limit, num_workgroups);
     if (st != SWIGLU_OK)
@@ -449,33 +694,34 @@ swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint1
         if (overlaps(out, in))
             return SWIGLU_ERR_INVALID_ARG;
 
-    DeviceLaunchInfo *info = nullptr;
-    hipError_t e = device_info(&info);
-    if (e != hipSuccess)
-        return fail_hip(e);
     const int vpr = (int)(inter / 8);
-    const int U = pick_u_fwd(vpr);
-    const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
-                                                                  info->fwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
-    switch (U) {
-    case 1: launch_fwd<1>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
-    case 2: launch_fwd<2>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
-    case 3: launch_fwd<3>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
-    default: launch_fwd<4>(blocks, stream, x, probs, y, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    if (num_workgroups != 0 || !launch_fwd_row(l, x, probs, y, rows, inter, limit, n_used, permutation_map, zp)) {
+        DeviceLaunchInfo *info = nullptr;
+        const hipError_t e = device_info(&info);
+        if (e != hipSuccess)
+            return fail_hip(e);
+        const int U = pick_u_fwd(vpr);
+        const int blocks = num_workgroups > 0 ? num_workgroups
+                                              : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
+                                                                      info->fwd_blocks_per_cu[U]);
+        const int r = (int)rows, n = (int)inter;
+        switch (U) {
+        case 1: launch_fwd<1>(l, blocks, x, probs, y, r, n, limit, n_used, permutation_map, zp); break;
+        case 2: launch_fwd<2>(l, blocks, x, probs, y, r, n, limit, n_used, permutation_map, zp); break;
+        case 3: launch_fwd<3>(l, blocks, x, probs, y, r, n, limit, n_used, permutation_map, zp); break;
+        default: launch_fwd<4>(l, blocks, x, probs, y, r, n, limit, n_used, permutation_map, zp); break;
+        }
     }
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail_hip(e);
     return SWIGLU_OK;
 }
 
-swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const uint16_t *grad_y,
-                                    uint16_t *grad_x, float *grad_probs,
-                                    int64_t rows, int64_t inter, float limit,
-                                    const int32_t *n_used, const int32_t *permutation_map,
-                                    int zero_padding, hipStream_t stream, int num_workgroups)
+swiglu_status_t bwd_impl(const uint16_t *x, const float *probs, const uint16_t *grad_y, uint16_t *grad_x,
+                         float *grad_probs, int64_t rows, int64_t inter, float limit, const int32_t *n_used,
+                         const int32_t *permutation_map, int zero_padding, int num_workgroups, const Launch &l)
 {
     swiglu_status_t st = check_shape(rows, inter, limit, num_workgroups);
     if (st != SWIGLU_OK)
@@ -498,35 +744,46 @@ swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const
     if (overlaps(outs[0], outs[1]))
         return SWIGLU_ERR_INVALID_ARG;
 
-    DeviceLaunchInfo *info = nullptr;
-    hipError_t e = device_info(&info);
-    if (e != hipSuccess)
-        return fail_hip(e);
     const int vpr = (int)(inter / 8);
-    const int U = pick_u_bwd(vpr);
-    const int blocks = num_workgroups > 0 ? num_workgroups
-                                          : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
-                                                                  info->bwd_blocks_per_cu[U]);
     const int zp = zero_padding ? 1 : 0;
-    switch (U) {
-    case 1: launch_bwd<1>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
-    case 2: launch_bwd<2>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
-    case 3: launch_bwd<3>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
-    default: launch_bwd<4>(blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows, (int)inter, limit, n_used, permutation_map, zp); break;
+    if (num_workgroups != 0 || !launch_bwd_lean(l, x, probs, grad_y, grad_x, grad_probs, rows, inter, limit,
+                                                n_used, permutation_map, zp)) {
+        DeviceLaunchInfo *info = nullptr;
+        const hipError_t e = device_info(&info);
+        if (e != hipSuccess)
+            return fail_hip(e);
+        const int U = pick_u_bwd(vpr);
+        const int blocks = num_workgroups > 0 ? num_workgroups
+                                              : split_walk_workgroups(rows, chunks_per_row(vpr, U), info->cus,
+                                                                      info->bwd_blocks_per_cu[U]);
+        const int r = (int)rows, n = (int)inter;
+        switch (U) {
+        case 1: launch_bwd<1>(l, blocks, x, probs, grad_y, grad_x, grad_probs, r, n, limit, n_used, permutation_map, zp); break;
+        case 2: launch_bwd<2>(l, blocks, x, probs, grad_y, grad_x, grad_probs, r, n, limit, n_used, permutation_map, zp); break;
+        case 3: launch_bwd<3>(l, blocks, x, probs, grad_y, grad_x, grad_probs, r, n, limit, n_used, permutation_map, zp); break;
+        default: launch_bwd<4>(l, blocks, x, probs, grad_y, grad_x, grad_probs, r, n, limit, n_used, permutation_map, zp); break;
+        }
     }
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail_hip(e);
     return SWIGLU_OK;
 }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
 
 swiglu_status_t swiglu_probs_fwd(const uint16_t *x, const float *probs, uint16_t *y,
                                  int64_t rows, int64_t inter, float limit,
                                  const int32_t *n_used, const int32_t *permutation_map,
                                  int zero_padding, hipStream_t stream)
 {
-    return swiglu_probs_fwd_ex(x, probs, y, rows, inter, limit, n_used, permutation_map,
-                               zero_padding, stream, 0);
+    return fwd_impl(x, probs, y, rows, inter, limit, n_used, permutation_map, zero_padding, 0,
+                    Launch{stream, nullptr, nullptr});
 }
 
 swiglu_status_t swiglu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
@@ -535,8 +792,48 @@ swiglu_status_t swiglu_probs_bwd(const uint16_t *x, const float *probs, const ui
                                  const int32_t *n_used, const int32_t *permutation_map,
                                  int zero_padding, hipStream_t stream)
 {
-    return swiglu_probs_bwd_ex(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, n_used,
-                               permutation_map, zero_padding, stream, 0);
+    return bwd_impl(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, n_used, permutation_map,
+                    zero_padding, 0, Launch{stream, nullptr, nullptr});
+}
+
+swiglu_status_t swiglu_probs_fwd_ex(const uint16_t *x, const float *probs, uint16_t *y,
+                                    int64_t rows, int64_t inter, float limit,
+                                    const int32_t *n_used, const int32_t *permutation_map,
+                                    int zero_padding, hipStream_t stream, int num_workgroups)
+{
+    return fwd_impl(x, probs, y, rows, inter, limit, n_used, permutation_map, zero_padding, num_workgroups,
+                    Launch{stream, nullptr, nullptr});
+}
+
+swiglu_status_t swiglu_probs_bwd_ex(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                    uint16_t *grad_x, float *grad_probs,
+                                    int64_t rows, int64_t inter, float limit,
+                                    const int32_t *n_used, const int32_t *permutation_map,
+                                    int zero_padding, hipStream_t stream, int num_workgroups)
+{
+    return bwd_impl(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, n_used, permutation_map,
+                    zero_padding, num_workgroups, Launch{stream, nullptr, nullptr});
+}
+
+swiglu_status_t swiglu_probs_fwd_timed(const uint16_t *x, const float *probs, uint16_t *y,
+                                       int64_t rows, int64_t inter, float limit,
+                                       const int32_t *n_used, const int32_t *permutation_map,
+                                       int zero_padding, hipStream_t stream, int num_workgroups,
+                                       hipEvent_t start, hipEvent_t stop)
+{
+    return fwd_impl(x, probs, y, rows, inter, limit, n_used, permutation_map, zero_padding, num_workgroups,
+                    Launch{stream, start, stop});
+}
+
+swiglu_status_t swiglu_probs_bwd_timed(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                       uint16_t *grad_x, float *grad_probs,
+                                       int64_t rows, int64_t inter, float limit,
+                                       const int32_t *n_used, const int32_t *permutation_map,
+                                       int zero_padding, hipStream_t stream, int num_workgroups,
+                                       hipEvent_t start, hipEvent_t stop)
+{
+    return bwd_impl(x, probs, grad_y, grad_x, grad_probs, rows, inter, limit, n_used, permutation_map,
+                    zero_padding, num_workgroups, Launch{stream, start, stop});
 }
 
 int swiglu_probs_default_workgroups(int direction, int64_t rows, int64_t inter)

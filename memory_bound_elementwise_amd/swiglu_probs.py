@@ -37,6 +37,10 @@ _SIGS = {
                             _vp, ctypes.c_int],
     "swiglu_probs_bwd_ex": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp,
                             ctypes.c_int, _vp, ctypes.c_int],
+    "swiglu_probs_fwd_timed": [_vp, _vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp, ctypes.c_int,
+                               _vp, ctypes.c_int, _vp, _vp],
+    "swiglu_probs_bwd_timed": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp,
+                               ctypes.c_int, _vp, ctypes.c_int, _vp, _vp],
     "swiglu_probs_default_workgroups": [ctypes.c_int, _i64, _i64],
     "swiglu_probs_status_string": [ctypes.c_int],
     "swiglu_probs_last_hip_error": [],
@@ -137,8 +141,11 @@ def _row_meta(rows, probs, n_used, permutation_map):
 def swiglu_probs_fwd(x: torch.Tensor, probs: torch.Tensor, y: torch.Tensor, limit: float, *,
                      n_used: Optional[torch.Tensor] = None,
                      permutation_map: Optional[torch.Tensor] = None, zero_padding: bool = False,
-                     stream=None, num_workgroups: int = 0) -> torch.Tensor:
-    """y = bf16(silu(clamp(gate, max=limit)) * clamp(up, -limit, limit) * probs), in place into ``y``."""
+                     stream=None, num_workgroups: int = 0, events=None) -> torch.Tensor:
+    """y = bf16(silu(clamp(gate, max=limit)) * clamp(up, -limit, limit) * probs), in place into ``y``.
+
+    ``events``: optional (start, stop) HIP event handles (ints) that record the kernel's own
+    start and end (swiglu_probs_fwd_timed); for benchmarks."""
     _bf16_2d(x, "x")
     _bf16_2d(y, "y")
     rows, two_inter = x.shape
@@ -147,9 +154,12 @@ def swiglu_probs_fwd(x: torch.Tensor, probs: torch.Tensor, y: torch.Tensor, limi
     _row_meta(rows, probs, n_used, permutation_map)
     dev = _on_device(x, probs, y, n_used, permutation_map)
     lib = load_library()
-    st = lib.swiglu_probs_fwd_ex(_ptr(x), _ptr(probs), _ptr(y), rows, two_inter // 2, float(limit),
-                                 _ptr(n_used), _ptr(permutation_map), int(bool(zero_padding)),
-                                 _stream(stream, dev), int(num_workgroups))
+    args = (_ptr(x), _ptr(probs), _ptr(y), rows, two_inter // 2, float(limit), _ptr(n_used),
+            _ptr(permutation_map), int(bool(zero_padding)), _stream(stream, dev), int(num_workgroups))
+    if events is None:
+        st = lib.swiglu_probs_fwd_ex(*args)
+    else:
+        st = lib.swiglu_probs_fwd_timed(*args, events[0], events[1])
     _check("swiglu_probs_fwd", st)
     return y
 
@@ -158,8 +168,10 @@ def swiglu_probs_bwd(x: torch.Tensor, probs: torch.Tensor, grad_y: torch.Tensor,
                      grad_x: torch.Tensor, grad_probs: Optional[torch.Tensor], limit: float, *,
                      n_used: Optional[torch.Tensor] = None,
                      permutation_map: Optional[torch.Tensor] = None, zero_padding: bool = False,
-                     stream=None, num_workgroups: int = 0):
-    """d_gate / d_up into the halves of ``grad_x``; per-slot probability gradient into ``grad_probs``."""
+                     stream=None, num_workgroups: int = 0, events=None):
+    """d_gate / d_up into the halves of ``grad_x``; per-slot probability gradient into ``grad_probs``.
+
+    ``events``: as for swiglu_probs_fwd (swiglu_probs_bwd_timed)."""
     _bf16_2d(x, "x")
     _bf16_2d(grad_y, "grad_y")
     _bf16_2d(grad_x, "grad_x")
@@ -172,10 +184,13 @@ def swiglu_probs_bwd(x: torch.Tensor, probs: torch.Tensor, grad_y: torch.Tensor,
         raise ValueError("grad_probs must be contiguous fp32 with one value per row")
     dev = _on_device(x, probs, grad_y, grad_x, grad_probs, n_used, permutation_map)
     lib = load_library()
-    st = lib.swiglu_probs_bwd_ex(_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x), _ptr(grad_probs),
-                                 rows, two_inter // 2, float(limit), _ptr(n_used),
-                                 _ptr(permutation_map), int(bool(zero_padding)),
-                                 _stream(stream, dev), int(num_workgroups))
+    args = (_ptr(x), _ptr(probs), _ptr(grad_y), _ptr(grad_x), _ptr(grad_probs), rows, two_inter // 2,
+            float(limit), _ptr(n_used), _ptr(permutation_map), int(bool(zero_padding)),
+            _stream(stream, dev), int(num_workgroups))
+    if events is None:
+        st = lib.swiglu_probs_bwd_ex(*args)
+    else:
+        st = lib.swiglu_probs_bwd_timed(*args, events[0], events[1])
     _check("swiglu_probs_bwd", st)
     return grad_x, grad_probs
 
@@ -186,14 +201,25 @@ def swiglu_probs_default_workgroups(direction: str, rows: int, inter: int) -> in
 
 
 # -- allocating conveniences and an autograd Function -------------------------
+def _new_output(shape, like: torch.Tensor, kw) -> torch.Tensor:
+    """An output the kernels write in full: rows that are not live (past n_used, or
+    dummy map entries) are written only with zero_padding, so otherwise they start as
+    zeros here rather than as whatever the allocation held."""
+    partial = (kw.get("n_used") is not None or kw.get("permutation_map") is not None) \
+        and not kw.get("zero_padding", False)
+    return (torch.zeros if partial else torch.empty)(shape, dtype=like.dtype, device=like.device)
+
+
 def forward(x: torch.Tensor, probs: torch.Tensor, limit: float, **kw) -> torch.Tensor:
-    y = torch.empty((x.shape[0], x.shape[1] // 2), dtype=x.dtype, device=x.device)
+    y = _new_output((x.shape[0], x.shape[1] // 2), x, kw)
     return swiglu_probs_fwd(x, probs, y, limit, **kw)
 
 
 def backward(x: torch.Tensor, probs: torch.Tensor, grad_y: torch.Tensor, limit: float, **kw):
-    grad_x = torch.empty_like(x)
-    grad_probs = torch.empty(probs.shape, dtype=torch.float32, device=x.device)
+    """(grad_x, grad_probs). grad_probs slots that no live row maps to are never written
+    by the kernel, so they start (and stay) zero: no probability gradient flows there."""
+    grad_x = _new_output(tuple(x.shape), x, kw)
+    grad_probs = torch.zeros(probs.shape, dtype=torch.float32, device=x.device)
     return swiglu_probs_bwd(x, probs, grad_y, grad_x, grad_probs, limit, **kw)
 
 

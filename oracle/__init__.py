@@ -42,13 +42,23 @@ _f64p = ctypes.POINTER(ctypes.c_double)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
 
-def default_threads() -> int:
-    """Host threads the oracle uses: every core this process may run on, at most 16."""
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: every core this process may run on, capped by
+    OMP_NUM_THREADS when that is set (a host shared between GPUs sets it to each GPU's
+    share of the cores), and by the library's limit of 256."""
+    n = host_cores()
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, min(256, n))
 
 
 def _ptr(a: Optional[np.ndarray], ptype):

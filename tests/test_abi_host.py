@@ -55,6 +55,7 @@ def test_library_exports_declared_symbols(built, header, lib):
 def test_swiglu_declarations_expected():
     names = declared_functions(os.path.join(ROOT, "include", "swiglu_probs.h"))
     for n in ("swiglu_probs_fwd", "swiglu_probs_bwd", "swiglu_probs_fwd_ex", "swiglu_probs_bwd_ex",
+              "swiglu_probs_fwd_timed", "swiglu_probs_bwd_timed",
               "swiglu_probs_status_string", "swiglu_probs_abi_version",
               "swiglu_probs_last_hip_error", "swiglu_probs_default_workgroups"):
         assert n in names

@@ -29,7 +29,7 @@ def _check_common(d, steps, warmup):
     assert d["unit"] == "GB/s" and d["value"] > 0 and d["ms_per_step"] > 0
     assert d["n_gpus"] == 1 and d["steps"] == steps and d["warmup"] == warmup
     assert d["higher_is_better"] is True and d["scaling"] in ("weak", "strong")
-    assert d["vs_baseline"] is None and d["dtype"] == "f32" and d["data"] == "synthetic"
+    assert d["vs_baseline"] is None and d["dtype"] == "bf16" and d["data"] == "synthetic"
     assert isinstance(d["metric"], str) and isinstance(d["config"]["workload"], str)
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
@@ -44,11 +44,18 @@ def test_headline_line():
     _check_common(d, 3, 2)
     assert d["config"]["workload"] == "headline"
     assert d["config"]["rows"] == 53760 and d["config"]["inter"] == 2048
-    assert d["roofline"]["kernel"] == "swiglu_probs_bwd_kernel"
+    assert d["roofline"]["kernel"] == "swiglu_probs_bwd"
     assert d["fwd"]["algorithmic_bytes"] == 660817920 and d["bwd"]["algorithmic_bytes"] == 1101434880
     assert abs(d["roofline"]["achieved"] - d["bwd"]["GB/s"]) < 0.2
-    assert set(d["hbm_probe"]) == {"copy_1r1w", "fwd_like_2r1w", "bwd_like_3r2w"}
-    assert d["cold"]["reps"] == 2
+    assert set(d["hbm_probe"]) == {"copy_1r1w", "fwd_like_2r1w", "bwd_like_3r2w", "torch_copy_1r1w",
+                                   "torch_add_2r1w", "hip_memcpy_1r1w"}
+    for name in ("fwd", "bwd"):
+        k = d[name]
+        # each launch's own start/end events: the durations are those of the kernel alone
+        assert 0 < k["us_min"] <= k["us"] <= k["us_max"] and k["us_back_to_back"] > 0
+        assert 0 < k["frac_of_best_ceiling"] < 1.5
+    assert d["device_ms_per_step"] > 0 and d["cold"]["reps"] == 2
+    assert d["cpu_baseline"]["host_cores"] >= d["cpu_baseline"]["cores"]
 
 
 def test_moe_op_line():

@@ -7,8 +7,8 @@ import torch
 from memory_bound_elementwise_amd import (SwigluProbs, SwigluProbsError, load_library,
                                           swiglu_probs_bwd, swiglu_probs_fwd)
 from memory_bound_elementwise_amd.workloads import make_inputs
-from parity import (compare_grad_probs, compare_rows, live_mask, run_oracle, say,
-                    to_dev_bits)
+from parity import (compare_grad_probs, compare_rows, grad_probs_violations, live_mask, run_oracle,
+                    say, slots_written, to_dev_bits, ulp_distance)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +77,45 @@ def test_autograd_function_matches_oracle():
                  "autograd grad_x")
     assert probs.grad.shape == probs.shape
     compare_grad_probs(probs.grad.reshape(-1).cpu().numpy(), rout, inp, "autograd grad_probs")
+
+
+@pytest.mark.parametrize("zero_padding", [False, True])
+def test_allocating_helpers_leave_no_stale_memory(zero_padding):
+    """forward() / backward() allocate their outputs. Rows that are not live (past the
+    device n_used, or dummy map entries) come back as zeros, written by the kernel with
+    zero_padding and zero-initialised otherwise; grad_probs slots that no live row maps
+    to stay zero, so no stale memory can reach an optimizer. Live rows match the oracle."""
+    from memory_bound_elementwise_amd.swiglu_probs import backward, forward
+    dev = torch.device("cuda:0")
+    inp = make_inputs("padded", seed=12, rows=1024)
+    pm = inp["permutation_map"].copy()
+    pm[[3, 77, 500]] = -1
+    inp["permutation_map"], inp["n_used"], inp["zero_padding"] = pm, 900, zero_padding
+    # dirty the allocator's cache so a fresh empty() would hand back non-zero memory
+    junk = torch.full((64 << 20,), -1, dtype=torch.int16, device=dev)
+    del junk
+    x = to_dev_bits(inp["x"], dev)
+    probs = torch.from_numpy(inp["probs"]).to(dev)
+    gy = to_dev_bits(inp["grad_y"], dev)
+    kw = dict(n_used=torch.tensor([900], dtype=torch.int32, device=dev),
+              permutation_map=torch.from_numpy(pm).to(dev), zero_padding=zero_padding)
+    y = forward(x, probs, inp["limit"], **kw)
+    gx, gp = backward(x, probs, gy, inp["limit"], **kw)
+    torch.cuda.synchronize()
+    ry, rout = run_oracle(inp)
+    live = np.zeros(1024, dtype=bool)
+    live[:900] = True
+    live[[3, 77, 500]] = False
+    yn = y.cpu().numpy().view(np.uint16)
+    gxn = gx.cpu().numpy().view(np.uint16)
+    assert ulp_distance(yn[live], ry[live]).max() <= 1, "forward() live rows beyond 1 bf16 ulp"
+    assert ulp_distance(gxn[live], rout["grad_x"][live]).max() <= 1, "backward() live rows beyond 1 bf16 ulp"
+    assert not yn[~live].any() and not gxn[~live].any(), "non-live rows are not zero"
+    gpn = gp.cpu().numpy()
+    written = slots_written(inp)
+    assert (~written).any() and not gpn[~written].any(), "grad_probs slots with no live row are not zero"
+    bad = grad_probs_violations(gpn[written], rout["grad_probs_f64"][written], rout["row_scale"][written])
+    assert bad.size == 0, f"backward() grad_probs: {bad.size} rows outside 1e-6 + 1e-5*S"
 
 
 def test_error_paths_write_nothing():

@@ -48,6 +48,29 @@ def test_grid_invariance_and_determinism():
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{what} bits changed with {nwg} workgroups"
 
 
+@pytest.mark.parametrize("inter,n_used,permute,zero_padding", [
+    (2048, None, False, False), (2048, 2500, True, True), (4096, 2500, True, False),
+    (1536, 2500, True, True), (1408, None, False, False), (2048 + 8, None, False, False)])
+def test_default_launch_matches_walks(inter, n_used, permute, zero_padding):
+    """The default launch runs straight-line kernels (a row per wave, or a row per
+    workgroup cut into four quarters); an explicit workgroup count runs the fixed-grid
+    walks. Every output bit, the row sums included, must be the same either way."""
+    from memory_bound_elementwise_amd.workloads import Workload
+    rows = 3001
+    w = Workload("walks", rows=rows, inter=inter, limit=7.0, x_std=3.0, probs="topk_softmax",
+                 n_used=n_used, permute=permute, zero_padding=zero_padding)
+    inp = make_inputs(w, seed=inter + 7)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ref = run_gpu(inp)
+    check_parity(inp, label=f"default launch inter={inter}")
+    for nwg in (1, 3, cus, 4 * cus, rows, -(-rows // 4)):
+        say(f"[walks] inter={inter} workgroups={nwg}")
+        got = run_gpu(inp, num_workgroups=nwg)
+        for a, b, what in zip(got, ref, ("y", "grad_x", "grad_probs")):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), \
+                f"{what} bits differ between the default launch and {nwg} workgroups"
+
+
 def test_row_subset_invariance():
     """A row's bits do not depend on the other rows in the launch (batch invariance)."""
     full = make_inputs("mid", seed=3, rows=600)

@@ -95,9 +95,10 @@ TRACE = os.path.join(ROOT, "profiles", "trace_swiglu_probs_headline.json")
 
 
 def trace_average(workload: str, key: str = "bwd", path: str = TRACE):
-    """Average kernel duration (us) of kernel `key` over the timed launches of the committed
-    rocprofv3 kernel trace of this bench, or None when it is missing, for another workload,
-    or taken on other kernel sources."""
+    """Kernel `key`'s durations from the committed rocprofv3 kernel trace of this bench:
+    rocprofv3's average over every call and the average over the launches that record
+    their own events (the ones fwd.us / bwd.us average here). None when the summary is
+    missing, for another workload, or taken on other kernel sources."""
     try:
         with open(path) as fh:
             d = json.load(fh)
@@ -105,7 +106,10 @@ def trace_average(workload: str, key: str = "bwd", path: str = TRACE):
         return None
     if d.get("workload") != workload or d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get(key, {}).get("average_us")
+    k = d.get(key)
+    if not k:
+        return None
+    return {"trace_us": k.get("average_us"), "trace_us_launch_event_steps": k.get("launch_event_steps_us")}
 
 
 def cpu_model() -> str:
@@ -675,7 +679,7 @@ def main() -> int:
                 "traffic": traffic,
                 "timing": "each launch records its own start and end (hipExtLaunchKernel events)"}
     if trace is not None:
-        roofline["trace_us"] = trace
+        roofline.update(trace)
     out = {
         "metric": METRIC,
         "value": round(value, 1),

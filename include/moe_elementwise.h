@@ -24,8 +24,9 @@
  *   - num_workgroups: 0 = the library's choice: one wave per row or block when a row
  *     is at most two column chunks (and always for the soft-clamped squared ReLU);
  *     one workgroup per row, its four waves sharing the row, for router-weight rows
- *     of four or more chunks; else persistent workgroups (one per CU) with the rows
- *     balanced over the waves. Never more than 16,777,215 workgroups (a dispatch
+ *     of four or more chunks; one wave per (token, column chunk) for the unpermute
+ *     with at most 8 local experts; else persistent workgroups (one per CU) with the
+ *     rows balanced over the waves. Never more than 16,777,215 workgroups (a dispatch
  *     holds its work-item count in 32 bits); the waves then take several rows each.
  *     An explicit count must lie in 1 .. 16,777,215; any count gives the same
  *     result bits.
@@ -66,11 +67,14 @@ typedef enum moe_status MOE_ENUM_BASE {
 } moe_status_t;
 
 /*
- * output = residual + round_to_dtype(expert_output + shared_expert_output)
- * The routed and shared expert outputs are added in fp32 and rounded to the
- * activation dtype before the residual is added (in fp32, rounded once), so the
- * result is bit-identical to the two unfused adds. The backward passes the output
- * gradient unchanged to all three inputs and needs no kernel.
+ * Fused MoE residual add (Megatron-Core "core.fusions.fused_moe_residual_add" page,
+ * fused_moe_residual_add and its kernel entry). Per element, in fp32:
+ *     s      = dtype(expert_output + shared_expert_output)
+ *     output = dtype(residual + s)
+ * where dtype() is one round-to-nearest-even to the tensors' dtype. These are the two
+ * roundings, in the same order, that two separate elementwise adds in that dtype make,
+ * so each output element equals theirs bit for bit. Its gradient reaches each of the
+ * three inputs unchanged; the backward launches nothing.
  *   num_elements: elements of each tensor, 0 <= num_elements <= 2^48.
  *   dtype: MOE_BF16, MOE_FP16 or MOE_FP32, the same for all four tensors.
  *   output may be the same pointer as one of the inputs (in place); any other
@@ -107,8 +111,8 @@ moe_status_t moe_router_weight_bwd(const void *grad_out, moe_dtype_t out_dtype, 
  * Squared ReLU x routing probability, forward, bf16 in and out.
  *   clamp != 0: c = clamp_scale * tanh(x / clamp_scale); y = bf16(relu(c)^2 * p), all
  *               in fp32 with one final rounding; clamp_scale must be finite and > 0.
- *               relu(c) is evaluated to 1.5e-6 relative (a rational form of tanh), so
- *               y is within 1 bf16 ulp of the exactly rounded value.
+ *               relu(c) is evaluated to 6.5e-5 relative (a rational form of tanh, under
+ *               2^-11), so y is within 1 bf16 ulp of the exactly rounded value.
  *   clamp == 0: y = bf16(bf16(relu(x)^2) * p): the square is rounded to bf16 first.
  *   x, y: [rows, hidden] bf16, hidden % 8 == 0; probs: fp32 [rows] indexed by slot.
  *   n_used, permutation_map, zero_padding: exactly as for swiglu_probs_fwd (device

@@ -323,6 +323,36 @@ __device__ __forceinline__ float row_sum_split(float (*part)[kWave], float acc, 
     return t;
 }
 
+// One row per wave (row = the wave's index in the grid), all `NCH` column chunks of it
+// loaded at once, for the default launch of rows of at most a couple of chunks: no walk,
+// no per-row bookkeeping beyond the row's own slot (row_slot) and probability
+// (load_row_prob). Op, the chunks' order and the row-sum order are walk_rows', so the
+// bits are the same as a walk over the same rows.
+template <int NCH, class Op>
+__device__ __forceinline__ void row_per_wave(Op &op, int rows, int flags, const int *__restrict__ n_used,
+                                             const int *__restrict__ perm, const float *__restrict__ probs)
+{
+    const int r = wave_id();
+    if (r >= rows)
+        return;
+    const int slot = row_slot(r, rows, flags, n_used, perm);
+    if (slot < 0 && !(flags & kZeroPadding))
+        return;
+    typename Op::Buf b[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        op.load(b[c], r, c, slot >= 0);
+    const float p = load_row_prob(probs, slot);
+    row_sum_reset(op);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        op.process(b[c], r, c, slot, p);
+    if constexpr (Op::kRowSum) {
+        if (slot >= 0 && op.row_sum_wanted())
+            op.store_row_sum(slot, wave_sum(op.acc));
+    }
+}
+
 // A workgroup's walk over its rows (row r, r + G, r + 2G, ... for workgroup r of G), the
 // four waves sharing each row: wave w takes the column chunks
 // [floor(w nch / 4), floor((w + 1) nch / 4)), at least one each for nch >= 4. With

@@ -356,18 +356,18 @@ __global__ __launch_bounds__(kBlock) void router_weight_bwd_kernel(const char *g
 // Squared ReLU x probs
 // ---------------------------------------------------------------------------
 // The soft clamp c = s * tanh(x / s) as x * R(u), u = (x / s)^2, with
-// R(u) = P(u) / Q(u) a (3,3) rational fitted minimax in relative error to tanh(z) / z
-// over 0 <= z <= 7.1 (coefficients from fit_tanh_rational.py beside this file).
-// Beyond z = 7.1, u is held at 7.1^2, so x * R grows past s and the clamp to s below
-// takes over; 1 - tanh(7.1) is 1.4e-6. Evaluated in fp32 this gives c to 1.5e-6
-// relative for every x, far inside half a bf16 ulp (2^-9), the one rounding the result
-// goes through. One reciprocal is the only quarter-rate operation: on this op the
-// vector ALU, not HBM, sets the pace.
-constexpr float kTanhP0 = 0.9999988675117493f, kTanhP1 = 0.12309558689594269f,
-                kTanhP2 = 0.002281768247485161f, kTanhP3 = 3.9414157981809694e-06f;
-constexpr float kTanhQ1 = 0.4564203917980194f, kTanhQ2 = 0.02109927497804165f,
-                kTanhQ3 = 0.00014274298155214638f;
-constexpr float kTanhUMax = 50.41f;
+// R(u) = P(u) / Q(u) a (2,2) rational fitted minimax in relative error to tanh(z) / z
+// over 0 <= z <= 5.2 (coefficients from fit_tanh_rational.py beside this file).
+// Beyond z = 5.2, u is held at 5.2^2, so x * R grows past s and the clamp to s below
+// takes over; 1 - tanh(5.2) is 6.1e-5. Evaluated in fp32 this gives c to 6.5e-5
+// relative for every x (so about 1.3e-4 on c^2), against 2^-8 for the one rounding
+// the result goes through: it moves no result by more than one bf16 ulp. Two fmas
+// fewer than a (3,3) fit to 1.5e-6, on the op whose pace the vector ALU sets; one
+// reciprocal is its only quarter-rate operation.
+constexpr float kTanhP0 = 0.9999353885650635f, kTanhP1 = 0.10179443657398224f,
+                kTanhP2 = 0.0006515600252896547f;
+constexpr float kTanhQ1 = 0.4347437024116516f, kTanhQ2 = 0.01262988243252039f;
+constexpr float kTanhUMax = 27.040000915527344f;
 
 // relu(s * tanh(x / s)) for s > 0. u stays finite (so no inf * 0 at x = +-inf: the
 // clamps give s and 0), and the NaN-propagating min / max keep a NaN input NaN, as
@@ -376,8 +376,8 @@ __device__ __forceinline__ float soft_clamp_relu(float x, float s, float inv_s)
 {
     const float z = x * inv_s;
     const float u = __builtin_fminf(z * z, kTanhUMax);
-    const float pn = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(kTanhP3, u, kTanhP2), u, kTanhP1), u, kTanhP0);
-    const float qd = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(kTanhQ3, u, kTanhQ2), u, kTanhQ1), u, 1.0f);
+    const float pn = __builtin_fmaf(__builtin_fmaf(kTanhP2, u, kTanhP1), u, kTanhP0);
+    const float qd = __builtin_fmaf(__builtin_fmaf(kTanhQ2, u, kTanhQ1), u, 1.0f);
     const float c = x * (pn * __builtin_amdgcn_rcpf(qd));
     return __builtin_elementwise_maximum(__builtin_elementwise_minimum(c, s), 0.0f);
 }
@@ -561,6 +561,28 @@ __global__ __launch_bounds__(kBlock) void squared_relu_probs_bwd_kernel(
     SquaredReluBwdOp<U, kClamp> op{x, g, gx, gp, hidden, s, inv_s, zero_padding,
                                    (uint32_t)lane_id() * kVecBytes, 0.0f};
     walk_rows(op, sched, perm, probs, nch);
+}
+
+// The default launches for rows of at most two chunks: one wave per row, the row's
+// chunks loaded at once (row_per_wave). Arguments ordered so the ones every wave needs
+// arrive preloaded; `flags` says which optional row arguments exist.
+template <int U, int NCH, bool kClamp>
+__global__ __launch_bounds__(kBlock) void squared_relu_probs_row_kernel(
+    int rows, int hidden, float s, float inv_s, int flags, const uint16_t *x, const float *probs, uint16_t *y,
+    const int *n_used, const int *perm)
+{
+    SquaredReluOp<U, kClamp> op{x, y, hidden, s, inv_s, flags & kZeroPadding, (uint32_t)lane_id() * kVecBytes};
+    row_per_wave<NCH>(op, rows, flags, n_used, perm, probs);
+}
+
+template <int U, int NCH, bool kClamp>
+__global__ __launch_bounds__(kBlock) void squared_relu_probs_bwd_row_kernel(
+    int rows, int hidden, float s, float inv_s, int flags, const uint16_t *x, const uint16_t *g, uint16_t *gx,
+    const float *probs, float *gp, const int *n_used, const int *perm)
+{
+    SquaredReluBwdOp<U, kClamp> op{x, g, gx, gp, hidden, s, inv_s, flags & kZeroPadding,
+                                   (uint32_t)lane_id() * kVecBytes, 0.0f};
+    row_per_wave<NCH>(op, rows, flags, n_used, perm, probs);
 }
 
 // ---------------------------------------------------------------------------
@@ -774,6 +796,109 @@ __global__ __launch_bounds__(kBlock) void unpermute_pipelined_kernel(const uint1
         c = n.c, j = n.j;
         if (t >= bound)
             break;
+    }
+}
+
+// The same reduction for up to 8 local experts with one wave per unit (token t, chunk
+// c), unit = t * nch + c, a grid of one wave per unit. The token's map row comes by
+// scalar loads; the contributing experts are compacted, in increasing expert id, into
+// the first K gather slots, and exactly those K gathers are issued (the kernel takes
+// a straight-line path per K, so every wait count is exact and no slot is empty); the
+// adds then run over the K slots in order. Skipping an absent expert is adding +0,
+// which changes no bit of the fp32 sum (it starts at +0 and is never -0), so the
+// result is the pipelined kernel's. With fp32 output the lanes hold the split layout
+// of the pipelined kernel.
+template <int ODT, int U, int K>
+__device__ __forceinline__ void unpermute_unit(const uint16_t *eo, const int (&rows)[8], char *out, int64_t t,
+                                               int c, int hidden)
+{
+    constexpr bool kSplit = ODT == DT_F32;
+    const int lane = lane_id();
+    const uint32_t row = (uint32_t)hidden * 2u;
+    const uint32_t chunk = (uint32_t)U * kWave * kVecBytes;
+    u32x4 b[K > 0 ? K : 1][U];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const rsrc_t rs = chunk_rsrc(eo + (int64_t)rows[k] * hidden, row, (uint32_t)c * chunk);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (kSplit) {
+                const uint32_t o = (uint32_t)u * kWave * kVecBytes + (uint32_t)lane * 8u;
+                const auto lo = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, kLoadAux);
+                const auto hi = __builtin_amdgcn_raw_buffer_load_b64(rs, o + kWave * 8u, 0, kLoadAux);
+                b[k][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                b[k][u] = load_vec(rs, (uint32_t)(lane + u * kWave) * kVecBytes);
+            }
+        }
+    }
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[u][i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[u][2 * q] = acc[u][2 * q] + bf16_lo(b[k][u][q]);
+                acc[u][2 * q + 1] = acc[u][2 * q + 1] + bf16_hi(b[k][u][q]);
+            }
+    const uint32_t orow = (uint32_t)hidden * kElemBytes<ODT>;
+    const rsrc_t ro = chunk_rsrc(out + t * orow, orow, (uint32_t)c * U * kWave * kOctBytes<ODT>);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (kSplit) {
+            const uint32_t o = (uint32_t)u * kWave * 32u + (uint32_t)lane * 16u;
+            store_vec(ro, u32x4{__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]),
+                                __float_as_uint(acc[u][2]), __float_as_uint(acc[u][3])}, o);
+            store_vec(ro, u32x4{__float_as_uint(acc[u][4]), __float_as_uint(acc[u][5]),
+                                __float_as_uint(acc[u][6]), __float_as_uint(acc[u][7])}, o + kWave * 16u);
+        } else {
+            store_oct<ODT>(ro, narrow<ODT>(acc[u]), (lane + u * kWave) * kOctBytes<ODT>);
+        }
+    }
+}
+
+template <int ODT, int U>
+__global__ __launch_bounds__(kBlock) void unpermute_unit_kernel(int tokens, int hidden, int E, int nch, int erows,
+                                                                const uint16_t *eo, const int *map, char *out,
+                                                                const int *valid_tokens)
+{
+    const int unit = wave_id();
+    const int t = unit / nch;
+    const int c = unit - t * nch;
+    if (t >= tokens)
+        return;
+    if (valid_tokens) {
+        const int v = *valid_tokens;
+        if (t >= v)  // also every token when v <= 0
+            return;
+    }
+    int rows[8];
+    int K = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        rows[e] = 0;
+        if (e < E) {
+            const int m = map[(int64_t)t * E + e];
+            if (m >= 0 && m < erows)
+                rows[K++] = m;
+        }
+    }
+    switch (K) {
+    case 0: unpermute_unit<ODT, U, 0>(eo, rows, out, t, c, hidden); break;
+    case 1: unpermute_unit<ODT, U, 1>(eo, rows, out, t, c, hidden); break;
+    case 2: unpermute_unit<ODT, U, 2>(eo, rows, out, t, c, hidden); break;
+    case 3: unpermute_unit<ODT, U, 3>(eo, rows, out, t, c, hidden); break;
+    case 4: unpermute_unit<ODT, U, 4>(eo, rows, out, t, c, hidden); break;
+    case 5: unpermute_unit<ODT, U, 5>(eo, rows, out, t, c, hidden); break;
+    case 6: unpermute_unit<ODT, U, 6>(eo, rows, out, t, c, hidden); break;
+    case 7: unpermute_unit<ODT, U, 7>(eo, rows, out, t, c, hidden); break;
+    default: unpermute_unit<ODT, U, 8>(eo, rows, out, t, c, hidden); break;
     }
 }
 
@@ -1011,6 +1136,8 @@ constexpr int kUnpermuteBlocksPerCU = 2;
 constexpr int kUnpermutePipelinedMaxExperts = 8;
 constexpr int kUnpermutePipeU = 2;
 constexpr int kUnpermutePipeBlocksPerCU = 1;
+// Octs per lane per chunk of the one-unit-per-wave unpermute.
+constexpr int kUnpermuteUnitU = 2;
 // The soft-clamped squared ReLU (forward ~19, backward ~30 vector instructions per
 // element) keeps the VALU 73% / 86% busy. It runs with 2 octs per lane per chunk
 // (83 registers, up to 6 waves per SIMD) and one wave per row whatever the row length.
@@ -1037,6 +1164,51 @@ int squared_relu_workgroups(int64_t rows, int64_t hidden, int cus, int clamp)
     if (clamp)
         return walk_workgroups(rows, 1, cus, 1);
     return walk_workgroups(rows, row_chunks(hidden / 8, squared_relu_u(hidden / 8, 0)), cus, 1);
+}
+
+int row_flags(int zp, const int32_t *n_used, const int32_t *perm)
+{
+    return (zp ? kZeroPadding : 0) | (n_used ? kHasNUsed : 0) | (perm ? kHasPerm : 0);
+}
+
+// The default launch of the squared ReLU when a row is one or two chunks and one wave
+// per row fits in a dispatch: the row kernels. Returns false (nothing launched) when
+// the shape takes the walk.
+template <bool C, int U, int NCH>
+void launch_sqrelu_row_un(bool bwd, hipStream_t st, int rows, int hidden, float s, float inv_s, int flags,
+                          const uint16_t *x, const uint16_t *g, uint16_t *out, const float *p, float *gp,
+                          const int *nu, const int *pm)
+{
+    const int blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (bwd)
+        hipLaunchKernelGGL((squared_relu_probs_bwd_row_kernel<U, NCH, C>), dim3(blocks), dim3(kBlock), 0, st, rows,
+                           hidden, s, inv_s, flags, x, g, out, p, gp, nu, pm);
+    else
+        hipLaunchKernelGGL((squared_relu_probs_row_kernel<U, NCH, C>), dim3(blocks), dim3(kBlock), 0, st, rows,
+                           hidden, s, inv_s, flags, x, p, out, nu, pm);
+}
+
+template <bool C>
+bool launch_sqrelu_row(bool bwd, int U, hipStream_t st, int64_t rows, int64_t hidden, float s, float inv_s,
+                       int flags, const uint16_t *x, const uint16_t *g, uint16_t *out, const float *p, float *gp,
+                       const int *nu, const int *pm)
+{
+    const int64_t nch = row_chunks(hidden / 8, U);
+    if (nch > 2 || (rows + kWavesPerBlock - 1) / kWavesPerBlock > kMaxWorkgroups)
+        return false;
+    const int r = (int)rows, h = (int)hidden;
+    const int key = U * 10 + (int)nch;
+    switch (key) {
+    case 11: launch_sqrelu_row_un<C, 1, 1>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 12: launch_sqrelu_row_un<C, 1, 2>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 21: launch_sqrelu_row_un<C, 2, 1>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 22: launch_sqrelu_row_un<C, 2, 2>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 31: launch_sqrelu_row_un<C, 3, 1>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 32: launch_sqrelu_row_un<C, 3, 2>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 41: launch_sqrelu_row_un<C, 4, 1>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    case 42: launch_sqrelu_row_un<C, 4, 2>(bwd, st, r, h, s, inv_s, flags, x, g, out, p, gp, nu, pm); return true;
+    default: return false;
+    }
 }
 
 }  // namespace
@@ -1185,8 +1357,15 @@ moe_status_t moe_squared_relu_probs_fwd(const uint16_t *x, const float *probs, u
     if (he != hipSuccess)
         return fail_hip(he);
     const int U = squared_relu_u(hidden / 8, clamp);
-    const int blocks = num_workgroups > 0 ? num_workgroups : squared_relu_workgroups(rows, hidden, cus, clamp);
     const float s = clamp ? clamp_scale : 1.0f;
+    const int flags = row_flags(zero_padding ? 1 : 0, n_used, permutation_map);
+    if (num_workgroups == 0 &&
+        (clamp ? launch_sqrelu_row<true>(false, U, stream, rows, hidden, s, 1.0f / s, flags, x, nullptr, y, probs,
+                                         nullptr, n_used, permutation_map)
+               : launch_sqrelu_row<false>(false, U, stream, rows, hidden, s, 1.0f, flags, x, nullptr, y, probs,
+                                          nullptr, n_used, permutation_map)))
+        return launched();
+    const int blocks = num_workgroups > 0 ? num_workgroups : squared_relu_workgroups(rows, hidden, cus, clamp);
     if (clamp)
         launch_sqrelu<true>(U, blocks, stream, x, probs, y, (int)rows, (int)hidden, s, 1.0f / s, n_used,
                             permutation_map, zero_padding ? 1 : 0);
@@ -1230,8 +1409,15 @@ moe_status_t moe_squared_relu_probs_bwd(const uint16_t *x, const float *probs, c
     if (he != hipSuccess)
         return fail_hip(he);
     const int U = squared_relu_u(hidden / 8, clamp);
-    const int blocks = num_workgroups > 0 ? num_workgroups : squared_relu_workgroups(rows, hidden, cus, clamp);
     const float s = clamp ? clamp_scale : 1.0f;
+    const int flags = row_flags(zero_padding ? 1 : 0, n_used, permutation_map);
+    if (num_workgroups == 0 &&
+        (clamp ? launch_sqrelu_row<true>(true, U, stream, rows, hidden, s, 1.0f / s, flags, x, grad_y, grad_x,
+                                         probs, grad_probs, n_used, permutation_map)
+               : launch_sqrelu_row<false>(true, U, stream, rows, hidden, s, 1.0f, flags, x, grad_y, grad_x,
+                                          probs, grad_probs, n_used, permutation_map)))
+        return launched();
+    const int blocks = num_workgroups > 0 ? num_workgroups : squared_relu_workgroups(rows, hidden, cus, clamp);
     if (clamp)
         launch_sqrelu_bwd<true>(U, blocks, stream, x, probs, grad_y, grad_x, grad_probs, (int)rows,
                                 (int)hidden, s, 1.0f / s, n_used, permutation_map, zero_padding ? 1 : 0);
@@ -1271,6 +1457,22 @@ moe_status_t moe_unpermute_expert_order(const uint16_t *expert_output, int64_t e
     hipError_t he = device_cus(&cus);
     if (he != hipSuccess)
         return fail_hip(he);
+    const int64_t units = tokens * row_chunks(hidden / 8, kUnpermuteUnitU);
+    if (num_workgroups == 0 && num_local_experts <= 8 &&
+        (units + kWavesPerBlock - 1) / kWavesPerBlock <= kMaxWorkgroups && units <= 0x7fffffffLL) {
+        const int blocks = (int)((units + kWavesPerBlock - 1) / kWavesPerBlock);
+        const int nch = (int)row_chunks(hidden / 8, kUnpermuteUnitU);
+        char *o = static_cast<char *>(out);
+        if (out_dtype == MOE_FP32)
+            hipLaunchKernelGGL((unpermute_unit_kernel<DT_F32, kUnpermuteUnitU>), dim3(blocks), dim3(kBlock), 0, stream,
+                               (int)tokens, (int)hidden, num_local_experts, nch, (int)expert_rows, expert_output,
+                               inverse_map, o, valid_tokens);
+        else
+            hipLaunchKernelGGL((unpermute_unit_kernel<DT_BF16, kUnpermuteUnitU>), dim3(blocks), dim3(kBlock), 0, stream,
+                               (int)tokens, (int)hidden, num_local_experts, nch, (int)expert_rows, expert_output,
+                               inverse_map, o, valid_tokens);
+        return launched();
+    }
     const bool pipelined = num_local_experts <= kUnpermutePipelinedMaxExperts;
     const int blocks = num_workgroups > 0 ? num_workgroups
                        : pipelined ? walk_workgroups(tokens, row_chunks(hidden / 8, kUnpermutePipeU), cus,

@@ -28,8 +28,8 @@ def _kernel_constants():
     src = open(os.path.join(CSRC, "moe_elementwise.hip")).read()
     vals = dict((k, np.float32(float(v))) for k, v in
                 re.findall(r"(kTanh[PQ]\d|kTanhUMax) = ([-+0-9.eE]+)f", src))
-    p = [vals[f"kTanhP{i}"] for i in range(4)]
-    q = [np.float32(1.0)] + [vals[f"kTanhQ{i}"] for i in range(1, 4)]
+    p = [vals[f"kTanhP{i}"] for i in range(3)]
+    q = [np.float32(1.0)] + [vals[f"kTanhQ{i}"] for i in range(1, 3)]
     return p, q, vals["kTanhUMax"]
 
 
@@ -37,17 +37,20 @@ def test_constants_come_from_the_fit():
     fit = _fit_module()
     p, q, umax = _kernel_constants()
     pf, qf, err = fit.fit(fit.ZMAX)
-    assert err < 1.5e-6
+    assert err < 7e-5 and 1 - np.tanh(fit.ZMAX) < 7e-5
     assert umax == np.float32(fit.ZMAX * fit.ZMAX)
     assert np.array_equal(np.asarray(p, np.float32), pf.astype(np.float32))
     assert np.array_equal(np.asarray(q, np.float32), qf.astype(np.float32))
 
 
 def test_fp32_evaluation_within_bound():
-    """1.5e-6 relative on c (so about 3e-6 on c^2): over 600 times inside half a bf16 ulp."""
+    """Under 2^-11 relative on c (6.5e-5 measured), so under 2^-10 on c^2: a result c^2 p
+    that far from the exact one rounds to a bf16 neighbour of the exact one's rounding (a
+    bf16 ulp is at least 2^-8 of the value), so it is within one ulp of the oracle."""
     fit = _fit_module()
     p, q, umax = _kernel_constants()
-    assert fit.worst_relative_error(p, q, umax) < 1.5e-6
+    err = fit.worst_relative_error(p, q, umax)
+    assert err < 2.0 ** -11 and err < 7e-5
 
 
 @pytest.mark.parametrize("s", [4.0, 0.5, 1e4])
@@ -66,11 +69,11 @@ def test_special_values(s):
 
 def test_nearly_monotone_and_saturating():
     """tanh is increasing. The minimax fit equioscillates, so the approximation may step
-    down, but by no more than twice its error bound, also where u is held at 7.1^2;
+    down, but by no more than twice its error bound, also where u is held at 5.2^2;
     and it reaches s."""
     fit = _fit_module()
     p, q, umax = _kernel_constants()
     x = np.linspace(0.0, 40.0, 400_001).astype(np.float32)
     got = fit.soft_clamp_relu_fp32(x, 4.0, p, q, umax).astype(np.float64)
-    assert np.diff(got).min() >= -3e-6 * 4.0
-    assert got[-1] == 4.0 and np.all(got[x >= 4.0 * 7.2] == 4.0)
+    assert np.diff(got).min() >= -1.4e-4 * 4.0
+    assert got[-1] == 4.0 and np.all(got[x >= 4.0 * 5.3] == 4.0)

@@ -12,7 +12,8 @@ file's header:
 * ``squared_relu_probs_bwd`` the chain rule through that forward (the page gives none)
 * ``unpermute``          same page (_unpermute_tokens_in_expert_order_kernel)
 
-Element types are "bf16", "f16" or "f32"; 16-bit arrays are uint16 bit patterns.
+Element types are "bf16", "f16" or "f32"; 16-bit arrays are uint16 bit patterns. Every
+call takes ``threads`` (default: ``oracle.default_threads()``); the bits do not depend on it.
 Pins: ``tests/moe_oracle_pins.py``.
 """
 from __future__ import annotations
@@ -24,6 +25,7 @@ from typing import Optional
 import numpy as np
 
 from . import build as _build
+from . import default_threads
 
 DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
 NP = {"bf16": np.uint16, "f16": np.uint16, "f32": np.float32}
@@ -52,17 +54,17 @@ class MoeOracle:
         lib = ctypes.CDLL(lib_path)
         lib.oracle_f16_from_f32.argtypes = [_vp, _vp, _i64]
         lib.oracle_f32_from_f16.argtypes = [_vp, _vp, _i64]
-        lib.oracle_residual_add.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.c_int]
-        lib.oracle_router_weight_fwd.argtypes = [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64]
-        lib.oracle_router_weight_bwd.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp,
-                                                 _vp, _vp, _i64, _i64]
-        lib.oracle_squared_relu_probs_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int,
-                                                      ctypes.c_float, _vp, _vp, ctypes.c_int]
+        _int = ctypes.c_int
+        lib.oracle_residual_add.argtypes = [_vp, _vp, _vp, _vp, _i64, _int, _int]
+        lib.oracle_router_weight_fwd.argtypes = [_vp, _int, _vp, _vp, _int, _i64, _i64, _int]
+        lib.oracle_router_weight_bwd.argtypes = [_vp, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp, _i64,
+                                                 _i64, _int]
+        lib.oracle_squared_relu_probs_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _int, ctypes.c_float,
+                                                      _vp, _vp, _int, _int]
         lib.oracle_squared_relu_probs_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
-                                                      ctypes.c_int, ctypes.c_float, _vp, _vp,
-                                                      ctypes.c_int]
-        lib.oracle_unpermute_expert_order.argtypes = [_vp, _i64, _vp, _vp, _vp, ctypes.c_int, _i64,
-                                                      _i64, _i64]
+                                                      _int, ctypes.c_float, _vp, _vp, _int, _int]
+        lib.oracle_unpermute_expert_order.argtypes = [_vp, _i64, _vp, _vp, _vp, _int, _i64, _i64, _i64,
+                                                      _int]
         for f in ("oracle_residual_add", "oracle_router_weight_fwd", "oracle_router_weight_bwd",
                   "oracle_squared_relu_probs_fwd", "oracle_squared_relu_probs_bwd",
                   "oracle_unpermute_expert_order"):
@@ -87,27 +89,28 @@ class MoeOracle:
         self.lib.oracle_f32_from_f16(_p(a), _p(out), a.size)
         return out
 
-    def residual_add(self, expert, shared, residual, dtype: str):
+    def residual_add(self, expert, shared, residual, dtype: str, threads: Optional[int] = None):
         e, s, r = (_c(v, NP[dtype]) for v in (expert, shared, residual))
         if not (e.shape == s.shape == r.shape):
             raise ValueError("shape mismatch")
         out = np.empty_like(e)
-        self._rc(self.lib.oracle_residual_add(_p(e), _p(s), _p(r), _p(out), e.size, DTYPES[dtype]),
-                 "oracle_residual_add")
+        self._rc(self.lib.oracle_residual_add(_p(e), _p(s), _p(r), _p(out), e.size, DTYPES[dtype],
+                                              threads or default_threads()), "oracle_residual_add")
         return out
 
-    def router_weight_fwd(self, x, x_dtype: str, probs, out_dtype: str):
+    def router_weight_fwd(self, x, x_dtype: str, probs, out_dtype: str, threads: Optional[int] = None):
         x = _c(x, NP[x_dtype])
         tokens, hidden = x.shape
         probs = _c(np.asarray(probs).reshape(-1), np.float32)
         out = np.empty((tokens, hidden), NP[out_dtype])
         self._rc(self.lib.oracle_router_weight_fwd(_p(x), DTYPES[x_dtype], _p(probs), _p(out),
-                                                   DTYPES[out_dtype], tokens, hidden),
+                                                   DTYPES[out_dtype], tokens, hidden,
+                                                   threads or default_threads()),
                  "oracle_router_weight_fwd")
         return out
 
     def router_weight_bwd(self, grad_out, out_dtype: str, x, x_dtype: str, probs,
-                          want_grad_x=True, want_grad_probs=True):
+                          want_grad_x=True, want_grad_probs=True, threads: Optional[int] = None):
         g = _c(grad_out, NP[out_dtype])
         tokens, hidden = g.shape
         probs = _c(np.asarray(probs).reshape(-1), np.float32)
@@ -120,11 +123,12 @@ class MoeOracle:
             sc = np.empty(tokens, np.float64)
         self._rc(self.lib.oracle_router_weight_bwd(_p(g), DTYPES[out_dtype], _p(xx), DTYPES[x_dtype],
                                                    _p(probs), _p(gx), _p(gp), _p(gp64), _p(sc),
-                                                   tokens, hidden), "oracle_router_weight_bwd")
+                                                   tokens, hidden, threads or default_threads()),
+                 "oracle_router_weight_bwd")
         return {"grad_x": gx, "grad_probs": gp, "grad_probs_f64": gp64, "row_scale": sc}
 
     def squared_relu_probs(self, x, probs, *, clamp_scale=None, n_used=None, permutation_map=None,
-                           zero_padding=False, out=None):
+                           zero_padding=False, out=None, threads: Optional[int] = None):
         x = _c(x, np.uint16)
         rows, hidden = x.shape
         probs = _c(np.asarray(probs).reshape(-1), np.float32)
@@ -134,13 +138,14 @@ class MoeOracle:
         clamp = clamp_scale is not None
         self._rc(self.lib.oracle_squared_relu_probs_fwd(_p(x), _p(probs), _p(y), rows, hidden,
                                                         int(clamp), float(clamp_scale or 0.0), _p(nu),
-                                                        _p(pm), int(bool(zero_padding))),
+                                                        _p(pm), int(bool(zero_padding)),
+                                                        threads or default_threads()),
                  "oracle_squared_relu_probs_fwd")
         return y
 
     def squared_relu_probs_bwd(self, x, probs, grad_y, *, clamp_scale=None, n_used=None,
                                permutation_map=None, zero_padding=False, grad_x_out=None,
-                               grad_probs_out=None, want_grad_x=True):
+                               grad_probs_out=None, want_grad_x=True, threads: Optional[int] = None):
         """grad_x (bf16 bits), grad_probs (fp32, slot-indexed), grad_probs_f64 and the row
         scale S = sum |g * y_pre| (both slot-indexed; NaN where a slot is not live)."""
         x = _c(x, np.uint16)
@@ -163,11 +168,12 @@ class MoeOracle:
         self._rc(self.lib.oracle_squared_relu_probs_bwd(_p(x), _p(probs), _p(g), _p(gx), _p(gp),
                                                         _p(gp64), _p(sc), rows, hidden, int(clamp),
                                                         float(clamp_scale or 0.0), _p(nu), _p(pm),
-                                                        int(bool(zero_padding))),
+                                                        int(bool(zero_padding)), threads or default_threads()),
                  "oracle_squared_relu_probs_bwd")
         return {"grad_x": gx, "grad_probs": gp, "grad_probs_f64": gp64, "row_scale": sc}
 
-    def unpermute(self, expert_output, inverse_map, out_dtype: str, *, valid_tokens=None, out=None):
+    def unpermute(self, expert_output, inverse_map, out_dtype: str, *, valid_tokens=None, out=None,
+                  threads: Optional[int] = None):
         eo = _c(expert_output, np.uint16)
         expert_rows, hidden = eo.shape
         im = _c(inverse_map, np.int32)
@@ -176,7 +182,8 @@ class MoeOracle:
             if out is None else _c(out, NP[out_dtype])
         vt = None if valid_tokens is None else np.array([valid_tokens], np.int32)
         self._rc(self.lib.oracle_unpermute_expert_order(_p(eo), expert_rows, _p(im), _p(vt), _p(o),
-                                                        DTYPES[out_dtype], tokens, hidden, n_exp),
+                                                        DTYPES[out_dtype], tokens, hidden, n_exp,
+                                                        threads or default_threads()),
                  "oracle_unpermute_expert_order")
         return o
 

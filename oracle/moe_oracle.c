@@ -27,10 +27,14 @@
  *
  * Every elementwise operation is written in the order the pages state it, with
  * separately rounded fp32 operations (built without fast-math or FMA contraction).
+ * Rows (tokens, or blocks of elements for the residual add) are split in static
+ * contiguous blocks over `threads` POSIX threads; every row's arithmetic is the same
+ * whichever thread runs it, so the results are bit-identical for any thread count.
  *
  * Element types: 0 = bf16, 1 = fp16, 2 = fp32 (16-bit types passed as bit patterns).
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -152,33 +156,154 @@ void oracle_f32_from_f16(const uint16_t *src, float *dst, int64_t n)
 }
 
 /* ---------------------------------------------------------------------------
+ * Static row blocks over POSIX threads
+ * ------------------------------------------------------------------------- */
+#define MOE_ORACLE_MAX_THREADS 256
+
+typedef struct {
+    const void *args;
+    int64_t r0, r1;
+    void (*body)(const void *, int64_t, int64_t);
+} row_block_t;
+
+static void *run_row_block(void *p)
+{
+    const row_block_t *b = (const row_block_t *)p;
+    b->body(b->args, b->r0, b->r1);
+    return NULL;
+}
+
+/* body(args, r0, r1) over [0, rows) in `threads` contiguous blocks (at most one per row). */
+static void over_rows(int64_t rows, int threads, const void *args, void (*body)(const void *, int64_t, int64_t))
+{
+    if (threads < 1)
+        threads = 1;
+    if (threads > MOE_ORACLE_MAX_THREADS)
+        threads = MOE_ORACLE_MAX_THREADS;
+    if ((int64_t)threads > rows)
+        threads = rows > 0 ? (int)rows : 1;
+    if (threads == 1) {
+        body(args, 0, rows);
+        return;
+    }
+    pthread_t tid[MOE_ORACLE_MAX_THREADS];
+    row_block_t blk[MOE_ORACLE_MAX_THREADS];
+    int started[MOE_ORACLE_MAX_THREADS];
+    int64_t per = rows / threads, extra = rows % threads, r = 0;
+    for (int t = 0; t < threads; ++t) {
+        const int64_t n = per + (t < extra ? 1 : 0);
+        blk[t] = (row_block_t){args, r, r + n, body};
+        r += n;
+        started[t] = pthread_create(&tid[t], NULL, run_row_block, &blk[t]) == 0;
+        if (!started[t])
+            run_row_block(&blk[t]); /* fall back to the calling thread */
+    }
+    for (int t = 0; t < threads; ++t)
+        if (started[t])
+            pthread_join(tid[t], NULL);
+}
+
+/* ---------------------------------------------------------------------------
  * Fused MoE residual add
  * ------------------------------------------------------------------------- */
+typedef struct {
+    const void *expert, *shared, *residual;
+    void *out;
+    int64_t n;
+    int dt;
+} residual_args_t;
+
+#define RESIDUAL_BLOCK 65536 /* elements per row block of the thread split */
+
+static void residual_rows(const void *p, int64_t b0, int64_t b1)
+{
+    const residual_args_t *A = (const residual_args_t *)p;
+    const int64_t i1 = b1 * RESIDUAL_BLOCK < A->n ? b1 * RESIDUAL_BLOCK : A->n;
+    for (int64_t i = b0 * RESIDUAL_BLOCK; i < i1; ++i) {
+        /* first add, rounded to the activation dtype; then the residual add */
+        float t = round_to(load_elem(A->expert, i, A->dt) + load_elem(A->shared, i, A->dt), A->dt);
+        store_elem(A->out, i, A->dt, load_elem(A->residual, i, A->dt) + t);
+    }
+}
+
 int oracle_residual_add(const void *expert, const void *shared, const void *residual, void *out,
-                        int64_t n, int dt)
+                        int64_t n, int dt, int threads)
 {
     if (n < 0 || dt < 0 || dt > 2)
         return 1;
-    for (int64_t i = 0; i < n; ++i) {
-        /* first add, rounded to the activation dtype; then the residual add */
-        float t = round_to(load_elem(expert, i, dt) + load_elem(shared, i, dt), dt);
-        store_elem(out, i, dt, load_elem(residual, i, dt) + t);
-    }
+    const residual_args_t a = {expert, shared, residual, out, n, dt};
+    over_rows((n + RESIDUAL_BLOCK - 1) / RESIDUAL_BLOCK, threads, &a, residual_rows);
     return 0;
 }
 
 /* ---------------------------------------------------------------------------
  * Router-weight multiply
  * ------------------------------------------------------------------------- */
+typedef struct {
+    const void *x;
+    int x_dt;
+    const float *probs;
+    void *out;
+    int out_dt;
+    int64_t hidden;
+} router_fwd_args_t;
+
+static void router_fwd_rows(const void *p, int64_t t0, int64_t t1)
+{
+    const router_fwd_args_t *A = (const router_fwd_args_t *)p;
+    const int64_t hidden = A->hidden;
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t h = 0; h < hidden; ++h)
+            store_elem(A->out, t * hidden + h, A->out_dt, load_elem(A->x, t * hidden + h, A->x_dt) * A->probs[t]);
+}
+
 int oracle_router_weight_fwd(const void *x, int x_dt, const float *probs, void *out, int out_dt,
-                             int64_t tokens, int64_t hidden)
+                             int64_t tokens, int64_t hidden, int threads)
 {
     if (tokens < 0 || hidden < 0)
         return 1;
-    for (int64_t t = 0; t < tokens; ++t)
-        for (int64_t h = 0; h < hidden; ++h)
-            store_elem(out, t * hidden + h, out_dt, load_elem(x, t * hidden + h, x_dt) * probs[t]);
+    const router_fwd_args_t a = {x, x_dt, probs, out, out_dt, hidden};
+    over_rows(tokens, threads, &a, router_fwd_rows);
     return 0;
+}
+
+/* grad_probs accumulated in fp64 in column order (and returned rounded to fp32),
+ * beside the row scale S = sum |g * x|; grad_x / grad_probs may be NULL. */
+typedef struct {
+    const void *grad_out;
+    int out_dt;
+    const void *x;
+    int x_dt;
+    const float *probs;
+    void *grad_x;
+    float *grad_probs;
+    double *grad_probs_f64, *row_scale;
+    int64_t hidden;
+} router_bwd_args_t;
+
+static void router_bwd_rows(const void *p, int64_t t0, int64_t t1)
+{
+    const router_bwd_args_t *A = (const router_bwd_args_t *)p;
+    const int64_t hidden = A->hidden;
+    for (int64_t t = t0; t < t1; ++t) {
+        double acc = 0.0, scale = 0.0;
+        for (int64_t h = 0; h < hidden; ++h) {
+            float g = load_elem(A->grad_out, t * hidden + h, A->out_dt);
+            if (A->grad_x)
+                store_elem(A->grad_x, t * hidden + h, A->x_dt, g * A->probs[t]);
+            if (A->grad_probs || A->grad_probs_f64 || A->row_scale) {
+                float term = g * load_elem(A->x, t * hidden + h, A->x_dt);
+                acc += (double)term;
+                scale += fabs((double)term);
+            }
+        }
+        if (A->grad_probs)
+            A->grad_probs[t] = (float)acc;
+        if (A->grad_probs_f64)
+            A->grad_probs_f64[t] = acc;
+        if (A->row_scale)
+            A->row_scale[t] = scale;
+    }
 }
 
 /* grad_probs accumulated in fp64 in column order (and returned rounded to fp32),
@@ -186,38 +311,70 @@ int oracle_router_weight_fwd(const void *x, int x_dt, const float *probs, void *
 int oracle_router_weight_bwd(const void *grad_out, int out_dt, const void *x, int x_dt,
                              const float *probs, void *grad_x, float *grad_probs,
                              double *grad_probs_f64, double *row_scale, int64_t tokens,
-                             int64_t hidden)
+                             int64_t hidden, int threads)
 {
     if (tokens < 0 || hidden < 0)
         return 1;
-    for (int64_t t = 0; t < tokens; ++t) {
-        double acc = 0.0, scale = 0.0;
-        for (int64_t h = 0; h < hidden; ++h) {
-            float g = load_elem(grad_out, t * hidden + h, out_dt);
-            if (grad_x)
-                store_elem(grad_x, t * hidden + h, x_dt, g * probs[t]);
-            if (grad_probs || grad_probs_f64 || row_scale) {
-                float term = g * load_elem(x, t * hidden + h, x_dt);
-                acc += (double)term;
-                scale += fabs((double)term);
-            }
-        }
-        if (grad_probs)
-            grad_probs[t] = (float)acc;
-        if (grad_probs_f64)
-            grad_probs_f64[t] = acc;
-        if (row_scale)
-            row_scale[t] = scale;
-    }
+    const router_bwd_args_t a = {grad_out, out_dt, x, x_dt, probs, grad_x, grad_probs, grad_probs_f64,
+                                 row_scale, hidden};
+    over_rows(tokens, threads, &a, router_bwd_rows);
     return 0;
 }
 
 /* ---------------------------------------------------------------------------
  * Squared ReLU x probs (forward), with the SwiGLU rows' bookkeeping
  * ------------------------------------------------------------------------- */
+typedef struct {
+    const uint16_t *x;
+    const float *probs;
+    uint16_t *y;
+    int64_t rows, hidden, bound;
+    int clamp;
+    float clamp_scale;
+    const int32_t *perm;
+    int zero_padding;
+} sqrelu_fwd_args_t;
+
+/* the slot of row r (-1 when not live): the SwiGLU rows' rules */
+static int64_t row_slot(int64_t r, int64_t rows, int64_t bound, const int32_t *perm)
+{
+    if (r >= bound)
+        return -1;
+    const int64_t slot = perm ? (int64_t)perm[r] : r;
+    return (slot < 0 || slot >= rows) ? -1 : slot;
+}
+
+static void sqrelu_fwd_rows(const void *p, int64_t r0, int64_t r1)
+{
+    const sqrelu_fwd_args_t *A = (const sqrelu_fwd_args_t *)p;
+    const int64_t hidden = A->hidden;
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t slot = row_slot(r, A->rows, A->bound, A->perm);
+        uint16_t *yr = A->y + r * hidden;
+        if (slot < 0) {
+            if (A->zero_padding)
+                memset(yr, 0, (size_t)hidden * sizeof(uint16_t));
+            continue;
+        }
+        const float p = A->probs[slot];
+        for (int64_t h = 0; h < hidden; ++h) {
+            float v = bf16_to_f32(A->x[r * hidden + h]);
+            if (A->clamp) {
+                float c = A->clamp_scale * tanhf(v / A->clamp_scale); /* soft clamp, fp32 */
+                float a = c < 0.0f ? 0.0f : c;                       /* relu; NaN passes, as torch.relu */
+                yr[h] = f32_to_bf16((a * a) * p);                     /* one rounding */
+            } else {
+                float a = v < 0.0f ? 0.0f : v;                        /* relu of bf16: bf16 */
+                float sq = bf16_to_f32(f32_to_bf16(a * a));           /* square materialised in bf16 */
+                yr[h] = f32_to_bf16(sq * p);
+            }
+        }
+    }
+}
+
 int oracle_squared_relu_probs_fwd(const uint16_t *x, const float *probs, uint16_t *y, int64_t rows,
                                   int64_t hidden, int clamp, float clamp_scale,
-                                  const int32_t *n_used, const int32_t *perm, int zero_padding)
+                                  const int32_t *n_used, const int32_t *perm, int zero_padding, int threads)
 {
     if (rows < 0 || hidden <= 0)
         return 1;
@@ -229,33 +386,8 @@ int oracle_squared_relu_probs_fwd(const uint16_t *x, const float *probs, uint16_
         if (bound > rows)
             bound = rows;
     }
-    for (int64_t r = 0; r < rows; ++r) {
-        int64_t slot = -1;
-        if (r < bound) {
-            slot = perm ? (int64_t)perm[r] : r;
-            if (slot < 0 || slot >= rows)
-                slot = -1;
-        }
-        uint16_t *yr = y + r * hidden;
-        if (slot < 0) {
-            if (zero_padding)
-                memset(yr, 0, (size_t)hidden * sizeof(uint16_t));
-            continue;
-        }
-        const float p = probs[slot];
-        for (int64_t h = 0; h < hidden; ++h) {
-            float v = bf16_to_f32(x[r * hidden + h]);
-            if (clamp) {
-                float c = clamp_scale * tanhf(v / clamp_scale); /* soft clamp, fp32 */
-                float a = c < 0.0f ? 0.0f : c;                  /* relu; NaN passes, as torch.relu */
-                yr[h] = f32_to_bf16((a * a) * p);                /* one rounding */
-            } else {
-                float a = v < 0.0f ? 0.0f : v;                  /* relu of bf16: bf16 */
-                float sq = bf16_to_f32(f32_to_bf16(a * a));     /* square materialised in bf16 */
-                yr[h] = f32_to_bf16(sq * p);
-            }
-        }
-    }
+    const sqrelu_fwd_args_t a = {x, probs, y, rows, hidden, bound, clamp, clamp_scale, perm, zero_padding};
+    over_rows(rows, threads, &a, sqrelu_fwd_rows);
     return 0;
 }
 
@@ -274,41 +406,39 @@ int oracle_squared_relu_probs_fwd(const uint16_t *x, const float *probs, uint16_
  * Rows follow the forward's rules; with zero_padding, grad_x of a row that is
  * not live is +0; grad_probs is written only for live slots.
  * ------------------------------------------------------------------------- */
-int oracle_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
-                                  uint16_t *grad_x, float *grad_probs, double *grad_probs_f64,
-                                  double *row_scale, int64_t rows, int64_t hidden, int clamp,
-                                  float clamp_scale, const int32_t *n_used, const int32_t *perm,
-                                  int zero_padding)
+typedef struct {
+    const uint16_t *x;
+    const float *probs;
+    const uint16_t *grad_y;
+    uint16_t *grad_x;
+    float *grad_probs;
+    double *grad_probs_f64, *row_scale;
+    int64_t rows, hidden, bound;
+    int clamp;
+    float clamp_scale;
+    const int32_t *perm;
+    int zero_padding;
+} sqrelu_bwd_args_t;
+
+static void sqrelu_bwd_rows(const void *p, int64_t r0, int64_t r1)
 {
-    if (rows < 0 || hidden <= 0)
-        return 1;
-    if (clamp && !(clamp_scale > 0.0f && isfinite(clamp_scale)))
-        return 1;
-    int64_t bound = rows;
-    if (n_used) {
-        bound = *n_used < 0 ? 0 : *n_used;
-        if (bound > rows)
-            bound = rows;
-    }
-    for (int64_t r = 0; r < rows; ++r) {
-        int64_t slot = -1;
-        if (r < bound) {
-            slot = perm ? (int64_t)perm[r] : r;
-            if (slot < 0 || slot >= rows)
-                slot = -1;
-        }
+    const sqrelu_bwd_args_t *A = (const sqrelu_bwd_args_t *)p;
+    const int64_t hidden = A->hidden;
+    const float clamp_scale = A->clamp_scale;
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t slot = row_slot(r, A->rows, A->bound, A->perm);
         if (slot < 0) {
-            if (zero_padding && grad_x)
-                memset(grad_x + r * hidden, 0, (size_t)hidden * sizeof(uint16_t));
+            if (A->zero_padding && A->grad_x)
+                memset(A->grad_x + r * hidden, 0, (size_t)hidden * sizeof(uint16_t));
             continue;
         }
-        const float prob = probs[slot]; /* gathered through the map */
+        const float prob = A->probs[slot]; /* gathered through the map */
         double acc = 0.0, scale = 0.0;
         for (int64_t h = 0; h < hidden; ++h) {
-            const float v = bf16_to_f32(x[r * hidden + h]);
-            const float g = bf16_to_f32(grad_y[r * hidden + h]);
+            const float v = bf16_to_f32(A->x[r * hidden + h]);
+            const float g = bf16_to_f32(A->grad_y[r * hidden + h]);
             float ypre, gx;
-            if (clamp) {
+            if (A->clamp) {
                 float z = v / clamp_scale;
                 float c = clamp_scale * tanhf(z);
                 float a = (c < 0.0f) ? 0.0f : c; /* relu; NaN passes */
@@ -321,19 +451,40 @@ int oracle_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const u
                 ypre = bf16_to_f32(f32_to_bf16(a * a));
                 gx = v > 0.0f ? (g * prob) * (2.0f * a) : 0.0f;
             }
-            if (grad_x)
-                grad_x[r * hidden + h] = f32_to_bf16(gx);
+            if (A->grad_x)
+                A->grad_x[r * hidden + h] = f32_to_bf16(gx);
             const float term = g * ypre;
             acc += (double)term;
             scale += fabs((double)term);
         }
-        if (grad_probs)
-            grad_probs[slot] = (float)acc;
-        if (grad_probs_f64)
-            grad_probs_f64[slot] = acc;
-        if (row_scale)
-            row_scale[slot] = scale;
+        if (A->grad_probs)
+            A->grad_probs[slot] = (float)acc;
+        if (A->grad_probs_f64)
+            A->grad_probs_f64[slot] = acc;
+        if (A->row_scale)
+            A->row_scale[slot] = scale;
     }
+}
+
+int oracle_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
+                                  uint16_t *grad_x, float *grad_probs, double *grad_probs_f64,
+                                  double *row_scale, int64_t rows, int64_t hidden, int clamp,
+                                  float clamp_scale, const int32_t *n_used, const int32_t *perm,
+                                  int zero_padding, int threads)
+{
+    if (rows < 0 || hidden <= 0)
+        return 1;
+    if (clamp && !(clamp_scale > 0.0f && isfinite(clamp_scale)))
+        return 1;
+    int64_t bound = rows;
+    if (n_used) {
+        bound = *n_used < 0 ? 0 : *n_used;
+        if (bound > rows)
+            bound = rows;
+    }
+    const sqrelu_bwd_args_t a = {x, probs, grad_y, grad_x, grad_probs, grad_probs_f64, row_scale,
+                                 rows, hidden, bound, clamp, clamp_scale, perm, zero_padding};
+    over_rows(rows, threads, &a, sqrelu_bwd_rows);
     return 0;
 }
 
@@ -344,10 +495,35 @@ int oracle_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const u
  * stored as fp32 or rounded once to bf16. Tokens t >= valid_tokens are neither read
  * nor written.
  * ------------------------------------------------------------------------- */
+typedef struct {
+    const uint16_t *expert_output;
+    int64_t expert_rows;
+    const int32_t *inverse_map;
+    void *out;
+    int out_dt;
+    int64_t hidden, num_local_experts;
+} unpermute_args_t;
+
+static void unpermute_rows(const void *p, int64_t t0, int64_t t1)
+{
+    const unpermute_args_t *A = (const unpermute_args_t *)p;
+    const int64_t hidden = A->hidden, E = A->num_local_experts;
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t h = 0; h < hidden; ++h) {
+            float acc = 0.0f;
+            for (int64_t e = 0; e < E; ++e) {
+                int64_t row = A->inverse_map[t * E + e];
+                if (row >= 0 && row < A->expert_rows)
+                    acc = acc + bf16_to_f32(A->expert_output[row * hidden + h]);
+            }
+            store_elem(A->out, t * hidden + h, A->out_dt, acc);
+        }
+}
+
 int oracle_unpermute_expert_order(const uint16_t *expert_output, int64_t expert_rows,
                                   const int32_t *inverse_map, const int32_t *valid_tokens,
                                   void *out, int out_dt, int64_t tokens, int64_t hidden,
-                                  int64_t num_local_experts)
+                                  int64_t num_local_experts, int threads)
 {
     if (tokens < 0 || hidden <= 0 || num_local_experts <= 0 || expert_rows < 0)
         return 1;
@@ -357,15 +533,7 @@ int oracle_unpermute_expert_order(const uint16_t *expert_output, int64_t expert_
         if (bound > tokens)
             bound = tokens;
     }
-    for (int64_t t = 0; t < bound; ++t)
-        for (int64_t h = 0; h < hidden; ++h) {
-            float acc = 0.0f;
-            for (int64_t e = 0; e < num_local_experts; ++e) {
-                int64_t row = inverse_map[t * num_local_experts + e];
-                if (row >= 0 && row < expert_rows)
-                    acc = acc + bf16_to_f32(expert_output[row * hidden + h]);
-            }
-            store_elem(out, t * hidden + h, out_dt, acc);
-        }
+    const unpermute_args_t a = {expert_output, expert_rows, inverse_map, out, out_dt, hidden, num_local_experts};
+    over_rows(bound, threads, &a, unpermute_rows);
     return 0;
 }

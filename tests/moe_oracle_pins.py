@@ -20,6 +20,8 @@ Each ``pin_*`` takes a ``MoeOracle`` and raises ``AssertionError`` on disagreeme
                           values), pin_squared_relu_bwd_rows (n_used / map / padding)
 * unpermute            -> pin_unpermute (numpy float32 running sums in expert order;
                           single-contribution tokens copy the row exactly; bounds)
+* row threads          -> pin_thread_count_invariance (every op, 1 thread against several:
+                          the same bits, padding and untouched slots included)
 """
 from __future__ import annotations
 
@@ -365,7 +367,44 @@ def pin_unpermute(orc):
     assert np.allclose(rev, fwd, rtol=0, atol=E * 2 * math.ldexp(1, -24) * np.abs(fwd).max() + 1e-30)
 
 
+def pin_thread_count_invariance(orc):
+    """Rows run in static blocks over threads; the arithmetic of a row does not depend on
+    which thread runs it, so every output bit is the same for 1, 3 and 7 threads (with
+    more row blocks than rows for the small cases, and a residual add large enough to
+    span several element blocks)."""
+    rng = np.random.default_rng(11)
+    rows, hidden = 203, 40
+    x = _draw((rows, hidden), "bf16", rng, 3.0)
+    g = _draw((rows, hidden), "bf16", rng, 1.0)
+    p = rng.random(rows).astype(np.float32)
+    m = rng.permutation(rows).astype(np.int32)
+    m[[4, 50]] = [-1, rows + 2]
+    n = 3 * 65536 + 17
+    e, sh, r = (_draw((n,), "bf16", rng, 1.0) for _ in range(3))
+    eo = _draw((300, hidden), "bf16", rng, 2.0, specials=False)
+    im = rng.integers(-1, 300, size=(rows, 8)).astype(np.int32)
+
+    def run(t):
+        outs = [orc.residual_add(e, sh, r, "bf16", threads=t),
+                orc.router_weight_fwd(x, "bf16", p, "f32", threads=t)]
+        rb = orc.router_weight_bwd(g, "bf16", x, "bf16", p, threads=t)
+        outs += [rb["grad_x"], rb["grad_probs"], rb["grad_probs_f64"], rb["row_scale"]]
+        for s in (None, 4.0):
+            outs.append(orc.squared_relu_probs(x, p, clamp_scale=s, n_used=190, permutation_map=m,
+                                               zero_padding=s is None, threads=t))
+            sb = orc.squared_relu_probs_bwd(x, p, g, clamp_scale=s, n_used=190, permutation_map=m,
+                                            zero_padding=s is not None, threads=t)
+            outs += [sb["grad_x"], sb["grad_probs"], sb["grad_probs_f64"], sb["row_scale"]]
+        outs += [orc.unpermute(eo, im, "f32", threads=t), orc.unpermute(eo, im, "bf16", valid_tokens=150, threads=t)]
+        return outs
+
+    ref = run(1)
+    for t in (3, 7):
+        for i, (a, b) in enumerate(zip(ref, run(t))):
+            assert a.tobytes() == b.tobytes(), f"output {i} changed with {t} threads"
+
+
 ALL_PINS = [pin_f16_conversions, pin_residual_add, pin_router_weight_fwd, pin_router_weight_bwd,
             pin_squared_relu_no_clamp, pin_squared_relu_clamp, pin_squared_relu_rows,
             pin_squared_relu_bwd_fd, pin_squared_relu_bwd_structure, pin_squared_relu_bwd_rows,
-            pin_unpermute]
+            pin_unpermute, pin_thread_count_invariance]

@@ -32,23 +32,24 @@ int oracle_swiglu_bwd_f64(const double *x, const double *probs, const double *gr
 void oracle_f16_from_f32(const float *src, uint16_t *dst, int64_t n);
 void oracle_f32_from_f16(const uint16_t *src, float *dst, int64_t n);
 int oracle_residual_add(const void *expert, const void *shared, const void *residual, void *out, int64_t n,
-                        int dt);
+                        int dt, int threads);
 int oracle_router_weight_fwd(const void *x, int x_dt, const float *probs, void *out, int out_dt, int64_t tokens,
-                             int64_t hidden);
+                             int64_t hidden, int threads);
 int oracle_router_weight_bwd(const void *grad_out, int out_dt, const void *x, int x_dt, const float *probs,
                              void *grad_x, float *grad_probs, double *grad_probs_f64, double *row_scale,
-                             int64_t tokens, int64_t hidden);
+                             int64_t tokens, int64_t hidden, int threads);
 int oracle_squared_relu_probs_fwd(const uint16_t *x, const float *probs, uint16_t *y, int64_t rows,
                                   int64_t hidden, int clamp, float clamp_scale, const int32_t *n_used,
-                                  const int32_t *perm, int zero_padding);
+                                  const int32_t *perm, int zero_padding, int threads);
 int oracle_squared_relu_probs_bwd(const uint16_t *x, const float *probs, const uint16_t *grad_y,
                                   uint16_t *grad_x, float *grad_probs, double *grad_probs_f64,
                                   double *row_scale, int64_t rows, int64_t hidden, int clamp,
                                   float clamp_scale, const int32_t *n_used, const int32_t *perm,
-                                  int zero_padding);
+                                  int zero_padding, int threads);
 int oracle_unpermute_expert_order(const uint16_t *expert_output, int64_t expert_rows,
                                   const int32_t *inverse_map, const int32_t *valid_tokens, void *out,
-                                  int out_dt, int64_t tokens, int64_t hidden, int64_t num_local_experts);
+                                  int out_dt, int64_t tokens, int64_t hidden, int64_t num_local_experts,
+                                  int threads);
 
 #define CHECK(cond, ...)                                                                  \
     do {                                                                                  \
@@ -228,22 +229,22 @@ static void drive_moe(void)
         const void *a = dt == 2 ? (const void *)a32 : a16, *b = dt == 2 ? (const void *)b32 : b16,
                    *c = dt == 2 ? (const void *)c32 : c16;
         void *o = dt == 2 ? (void *)o32 : o16;
-        CHECK(oracle_residual_add(a, b, c, o, T * H - 3, dt) == 0, "residual add dt %d", dt);
-        CHECK(oracle_residual_add(a, b, c, o, 0, dt) == 0, "residual add n 0");
+        CHECK(oracle_residual_add(a, b, c, o, T * H - 3, dt, 3) == 0, "residual add dt %d", dt);
+        CHECK(oracle_residual_add(a, b, c, o, 0, dt, 3) == 0, "residual add n 0");
         for (int odt = 0; odt < 3; ++odt) {
             if (!(odt == dt || odt == 2))
                 continue;
             const void *g = odt == 2 ? (const void *)b32 : b16;
             void *out = odt == 2 ? (void *)o32 : o16;
             void *gx = dt == 2 ? (void *)c32 : c16;
-            CHECK(oracle_router_weight_fwd(a, dt, p, out, odt, T, H) == 0, "router fwd");
-            CHECK(oracle_router_weight_bwd(g, odt, a, dt, p, gx, gp, gp64, scale, T, H) == 0, "router bwd");
-            CHECK(oracle_router_weight_bwd(g, odt, NULL, dt, p, gx, NULL, NULL, NULL, T, H) == 0, "router bwd gx only");
+            CHECK(oracle_router_weight_fwd(a, dt, p, out, odt, T, H, 3) == 0, "router fwd");
+            CHECK(oracle_router_weight_bwd(g, odt, a, dt, p, gx, gp, gp64, scale, T, H, 3) == 0, "router bwd");
+            CHECK(oracle_router_weight_bwd(g, odt, NULL, dt, p, gx, NULL, NULL, NULL, T, H, 2) == 0, "router bwd gx only");
         }
     }
-    CHECK(oracle_residual_add(a16, b16, c16, o16, -1, 0) != 0 && oracle_residual_add(a16, b16, c16, o16, 4, 3) != 0,
+    CHECK(oracle_residual_add(a16, b16, c16, o16, -1, 0, 1) != 0 && oracle_residual_add(a16, b16, c16, o16, 4, 3, 1) != 0,
           "bad residual add accepted");
-    CHECK(oracle_router_weight_fwd(a16, 0, p, o16, 0, -1, H) != 0, "bad router accepted");
+    CHECK(oracle_router_weight_fwd(a16, 0, p, o16, 0, -1, H, 1) != 0, "bad router accepted");
 
     /* squared ReLU forward and backward over the row rules, with and without the clamp */
     const int64_t SH = 16;
@@ -266,10 +267,10 @@ static void drive_moe(void)
                         const int32_t *mp = pm ? perm : NULL;
                         memset(y, 0xAB, ROWS * SH * 2);
                         memset(gx, 0xAB, ROWS * SH * 2);
-                        CHECK(oracle_squared_relu_probs_fwd(x, sp, y, ROWS, SH, clamp, scales[si], nu, mp, zp) == 0,
+                        CHECK(oracle_squared_relu_probs_fwd(x, sp, y, ROWS, SH, clamp, scales[si], nu, mp, zp, 3) == 0,
                               "sqrelu fwd");
                         CHECK(oracle_squared_relu_probs_bwd(x, sp, gy, gx, sgp, sgp64, sscale, ROWS, SH, clamp,
-                                                            scales[si], nu, mp, zp) == 0,
+                                                            scales[si], nu, mp, zp, 3) == 0,
                               "sqrelu bwd");
                         for (int r = 0; r < ROWS; ++r)
                             if (!live(r, nu, mp)) {
@@ -278,8 +279,8 @@ static void drive_moe(void)
                                       "sqrelu row %d not live: wrong contents", r);
                             }
                     }
-    CHECK(oracle_squared_relu_probs_fwd(x, sp, y, ROWS, SH, 1, 0.0f, NULL, NULL, 0) != 0, "clamp scale 0 accepted");
-    CHECK(oracle_squared_relu_probs_bwd(x, sp, gy, gx, sgp, NULL, NULL, ROWS, SH, 1, INFINITY, NULL, NULL, 0) != 0,
+    CHECK(oracle_squared_relu_probs_fwd(x, sp, y, ROWS, SH, 1, 0.0f, NULL, NULL, 0, 1) != 0, "clamp scale 0 accepted");
+    CHECK(oracle_squared_relu_probs_bwd(x, sp, gy, gx, sgp, NULL, NULL, ROWS, SH, 1, INFINITY, NULL, NULL, 0, 1) != 0,
           "infinite clamp scale accepted");
 
     /* unpermute: 1 to 8 experts, maps with invalid entries, a valid_tokens bound, both outputs */
@@ -298,16 +299,16 @@ static void drive_moe(void)
             const int32_t *vt = vi < 0 ? NULL : &valid[vi];
             memset(u32, 0xAB, UT * UH * 4);
             memset(u16, 0xAB, UT * UH * 2);
-            CHECK(oracle_unpermute_expert_order(eo, ER, map, vt, u32, 2, UT, UH, E) == 0, "unpermute f32");
-            CHECK(oracle_unpermute_expert_order(eo, ER, map, vt, u16, 0, UT, UH, E) == 0, "unpermute bf16");
+            CHECK(oracle_unpermute_expert_order(eo, ER, map, vt, u32, 2, UT, UH, E, 3) == 0, "unpermute f32");
+            CHECK(oracle_unpermute_expert_order(eo, ER, map, vt, u16, 0, UT, UH, E, 3) == 0, "unpermute bf16");
             int bound = (int)UT;
             if (vt)
                 bound = *vt < 0 ? 0 : (*vt > UT ? (int)UT : *vt);
             for (int64_t t = bound; t < UT; ++t)
                 CHECK(all16(u16 + t * UH, UH, 0xABAB), "unpermute wrote past valid_tokens");
         }
-    CHECK(oracle_unpermute_expert_order(eo, ER, map, NULL, u32, 2, UT, UH, 0) != 0, "zero experts accepted");
-    CHECK(oracle_unpermute_expert_order(eo, 0, map, NULL, u32, 2, UT, UH, 2) == 0, "no expert rows");
+    CHECK(oracle_unpermute_expert_order(eo, ER, map, NULL, u32, 2, UT, UH, 0, 1) != 0, "zero experts accepted");
+    CHECK(oracle_unpermute_expert_order(eo, 0, map, NULL, u32, 2, UT, UH, 2, 2) == 0, "no expert rows");
 
     free(a16), free(b16), free(c16), free(o16), free(a32), free(b32), free(c32), free(o32), free(p), free(gp);
     free(gp64), free(scale), free(x), free(gy), free(y), free(gx), free(sp), free(sgp), free(sgp64), free(sscale);

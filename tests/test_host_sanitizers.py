@@ -61,10 +61,10 @@ def test_a_planted_overrun_is_reported(tmp_path):
     """Plant a one-past-the-end write (the router-weight forward's column loop running
     to <= hidden) in a copy of the oracle: AddressSanitizer must stop the drive."""
     src = open(ORACLE_SOURCES[1]).read()
-    needle = "for (int64_t h = 0; h < hidden; ++h)\n            store_elem(out"
+    needle = "for (int64_t h = 0; h < hidden; ++h)\n            store_elem(A->out"
     assert src.count(needle) == 1, "the planted mistake no longer matches the oracle source"
     planted = tmp_path / "moe_oracle_planted.c"
-    planted.write_text(src.replace(needle, "for (int64_t h = 0; h <= hidden; ++h)\n            store_elem(out"))
+    planted.write_text(src.replace(needle, "for (int64_t h = 0; h <= hidden; ++h)\n            store_elem(A->out"))
     exe = str(tmp_path / "oracle_drive_planted")
     _build_oracle_drive(exe, [ORACLE_SOURCES[0], str(planted)])
     res = _run([exe], timeout=300)
@@ -83,17 +83,22 @@ def test_oracle_threads_under_tsan(tmp_path):
     assert "oracle sanitizer drive: ok" in res.stdout and "ThreadSanitizer" not in res.stderr
 
 
-def test_a_planted_race_is_reported(tmp_path):
+@pytest.mark.parametrize("which,needle,planted_text", [
+    (0, "blk[t].r1 = r + n;", "blk[t].r1 = r + n + (t + 1 < threads);"),
+    (1, "blk[t] = (row_block_t){args, r, r + n, body};", "blk[t] = (row_block_t){args, r, r + n + (t + 1 < threads), body};"),
+], ids=["swiglu_oracle", "moe_oracle"])
+def test_a_planted_race_is_reported(tmp_path, which, needle, planted_text):
     """Let each thread's block of rows run one row into the next thread's (the last
     block stays in range): two threads then write that row's outputs unordered, and
-    ThreadSanitizer must report it."""
-    src = open(ORACLE_SOURCES[0]).read()
-    needle = "blk[t].r1 = r + n;"
+    ThreadSanitizer must report it (for each oracle's thread split)."""
+    src = open(ORACLE_SOURCES[which]).read()
     assert src.count(needle) == 1, "the planted race no longer matches the oracle source"
-    planted = tmp_path / "swiglu_oracle_planted.c"
-    planted.write_text(src.replace(needle, "blk[t].r1 = r + n + (t + 1 < threads);"))
+    planted = tmp_path / "oracle_planted.c"
+    planted.write_text(src.replace(needle, planted_text))
     exe = str(tmp_path / "oracle_drive_race")
-    _build_oracle_drive(exe, [str(planted), ORACLE_SOURCES[1]], CFLAGS_TSAN)
+    sources = list(ORACLE_SOURCES)
+    sources[which] = str(planted)
+    _build_oracle_drive(exe, sources, CFLAGS_TSAN)
     res = _run([exe], timeout=300)
     assert res.returncode != 0
     assert "ThreadSanitizer: data race" in res.stderr, res.stderr[-3000:]

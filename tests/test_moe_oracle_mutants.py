@@ -12,21 +12,23 @@ from moe_oracle_pins import ALL_PINS
 
 MUTANTS = [
     ("residual_no_inner_rounding",
-     "float t = round_to(load_elem(expert, i, dt) + load_elem(shared, i, dt), dt);",
-     "float t = load_elem(expert, i, dt) + load_elem(shared, i, dt);"),
+     "float t = round_to(load_elem(A->expert, i, A->dt) + load_elem(A->shared, i, A->dt), A->dt);",
+     "float t = load_elem(A->expert, i, A->dt) + load_elem(A->shared, i, A->dt);"),
     ("residual_wrong_operand",
-     "float t = round_to(load_elem(expert, i, dt) + load_elem(shared, i, dt), dt);",
-     "float t = round_to(load_elem(expert, i, dt) + load_elem(residual, i, dt), dt);"),
+     "float t = round_to(load_elem(A->expert, i, A->dt) + load_elem(A->shared, i, A->dt), A->dt);",
+     "float t = round_to(load_elem(A->expert, i, A->dt) + load_elem(A->residual, i, A->dt), A->dt);"),
     ("f16_ties_away", "    float r = nearbyintf(n);\n    if (r == 2048.0f)", "    float r = roundf(n);\n    if (r == 2048.0f)"),
     ("f16_subnormal_truncated", "float r = nearbyintf(n);   /* default", "float r = truncf(n);   /* default"),
-    ("router_fwd_wrong_prob", "load_elem(x, t * hidden + h, x_dt) * probs[t]);", "load_elem(x, t * hidden + h, x_dt) * probs[0]);"),
-    ("router_grad_x_no_prob", "store_elem(grad_x, t * hidden + h, x_dt, g * probs[t]);", "store_elem(grad_x, t * hidden + h, x_dt, g);"),
-    ("router_grad_probs_times_p", "float term = g * load_elem(x, t * hidden + h, x_dt);",
-     "float term = g * load_elem(x, t * hidden + h, x_dt) * probs[t];"),
+    ("router_fwd_wrong_prob", "load_elem(A->x, t * hidden + h, A->x_dt) * A->probs[t]);",
+     "load_elem(A->x, t * hidden + h, A->x_dt) * A->probs[0]);"),
+    ("router_grad_x_no_prob", "store_elem(A->grad_x, t * hidden + h, A->x_dt, g * A->probs[t]);",
+     "store_elem(A->grad_x, t * hidden + h, A->x_dt, g);"),
+    ("router_grad_probs_times_p", "float term = g * load_elem(A->x, t * hidden + h, A->x_dt);",
+     "float term = g * load_elem(A->x, t * hidden + h, A->x_dt) * A->probs[t];"),
     ("sqrelu_square_not_rounded", "float sq = bf16_to_f32(f32_to_bf16(a * a));", "float sq = a * a;"),
-    ("sqrelu_scale_inverted", "tanhf(v / clamp_scale)", "tanhf(v * clamp_scale)"),
+    ("sqrelu_scale_inverted", "tanhf(v / A->clamp_scale)", "tanhf(v * A->clamp_scale)"),
     ("sqrelu_no_relu", "float a = c < 0.0f ? 0.0f : c;", "float a = c;"),
-    ("sqrelu_map_not_gathered", "const float p = probs[slot];", "const float p = probs[r];"),
+    ("sqrelu_map_not_gathered", "const float p = A->probs[slot];", "const float p = A->probs[r];"),
     ("sqrelu_bwd_no_factor_two", "((g * prob) * (2.0f * a)) * sech2", "((g * prob) * a) * sech2"),
     ("sqrelu_bwd_sech2_from_fp32_tanh", "float sech2 = (4.0f * e) / ((1.0f + e) * (1.0f + e));",
      "float sech2 = 1.0f - tanhf(z) * tanhf(z);"),
@@ -38,11 +40,14 @@ MUTANTS = [
     ("sqrelu_bwd_no_relu", "float a = (c < 0.0f) ? 0.0f : c; /* relu; NaN passes */", "float a = c;"),
     ("sqrelu_bwd_grad_probs_times_p", "const float term = g * ypre;", "const float term = g * ypre * prob;"),
     ("sqrelu_bwd_square_not_rounded", "ypre = bf16_to_f32(f32_to_bf16(a * a));", "ypre = a * a;"),
-    ("sqrelu_bwd_no_gather", "const float prob = probs[slot];", "const float prob = probs[r];"),
-    ("sqrelu_bwd_padding_not_zeroed", "if (zero_padding && grad_x)", "if (0 && grad_x)"),
-    ("unpermute_reversed", "for (int64_t e = 0; e < num_local_experts; ++e) {",
-     "for (int64_t e = num_local_experts - 1; e >= 0; --e) {"),
-    ("unpermute_bound_off_by_one", "for (int64_t t = 0; t < bound; ++t)", "for (int64_t t = 0; t < bound + (bound < tokens); ++t)"),
+    ("sqrelu_bwd_no_gather", "const float prob = A->probs[slot];", "const float prob = A->probs[r];"),
+    ("sqrelu_bwd_padding_not_zeroed", "if (A->zero_padding && A->grad_x)", "if (0 && A->grad_x)"),
+    ("unpermute_reversed", "for (int64_t e = 0; e < E; ++e) {", "for (int64_t e = E - 1; e >= 0; --e) {"),
+    ("unpermute_bound_off_by_one", "over_rows(bound, threads, &a, unpermute_rows);",
+     "over_rows(bound + (bound < tokens), threads, &a, unpermute_rows);"),
+    # a thread's row block one row short: results then depend on the thread count
+    ("thread_blocks_drop_a_row", "blk[t] = (row_block_t){args, r, r + n, body};",
+     "blk[t] = (row_block_t){args, r, r + n - (t > 0 && n > 1), body};"),
 ]
 
 

@@ -34,6 +34,9 @@ Printed JSON line (stdout):
                3:2 read:write) and, sharing no code with the kernels, torch copy_, a bf16
                torch.add and hipMemcpyDtoDAsync. With --op, the probe at each kernel's
                own read:write mix and size, and the kernel's fraction of it
+With --op (a MoE operation), the step is that op's kernels in order; kernels.<name>.us is
+the kernel alone back to back, timed the same way as its probe (time_windows), and cold_*
+as above.
   cpu_baseline the CPU oracle (test infrastructure, untuned) on the same inputs,
                timed on this host's cores (cores = threads used, host_cores = the
                process's CPU affinity)
@@ -201,34 +204,33 @@ class TimingEvents:
 
 def time_kernels(kernels, steps, warmup, cold_reps):
     """kernels: list of (name, launch), one step being each launched once in order.
-    Returns wall ms per step, per-kernel event times (lists, ms) over the timed steps,
-    and cold (median, min) ms per kernel (empty when cold_reps is 0).
+    Returns (wall ms per step, device ms per step, {name: ms per launch back to back},
+    {name: (median, min) cold ms}) (the last empty when cold_reps is 0).
 
-    One event is recorded before the first launch and one after every launch, on the
-    launch stream, so each launch lies between two events and consecutive launches
-    share the one between them. Each recorded event costs the stream time (on MI355X,
-    with torch's default events, 2 per fwd+bwd step instead of 3 took the step from 283
-    to 278 us; with none it was 272 us), so no more are recorded than the per-launch
-    durations need, and they are TimingEvents, which skip the system-scope fence."""
+    The step timing has no event between the kernels: two stream events bracket the
+    `steps` timed steps (each event costs the stream several microseconds on MI355X,
+    about as long as a small kernel's tail). Each kernel is then timed alone by
+    time_windows, the same back-to-back windows the streaming probe is timed with, so
+    kernel and probe figures compare like with like. Cold launches are timed one at a
+    time, each after a cache-evicting read, between two events."""
     import numpy as np
     import torch
     for _ in range(warmup):
         for _, fn in kernels:
             fn()
     torch.cuda.synchronize()
-    n = len(kernels)
-    ev = TimingEvents(steps * n + 1)
+    sev = TimingEvents(2)
     t0 = time.perf_counter()
-    ev.record(0)
-    for s in range(steps):
-        for i, (_, fn) in enumerate(kernels):
+    sev.record(0)
+    for _ in range(steps):
+        for _, fn in kernels:
             fn()
-            ev.record(s * n + i + 1)
+    sev.record(1)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = {name: [ev.elapsed_ms(s * n + i, s * n + i + 1) for s in range(steps)]
-           for i, (name, _) in enumerate(kernels)}
-    ev.close()
+    dev_ms = sev.elapsed_ms(0, 1) / steps
+    sev.close()
+    per = {name: time_windows(fn) for name, fn in kernels}
     cold = {}
     if cold_reps > 0:
         evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
@@ -246,7 +248,7 @@ def time_kernels(kernels, steps, warmup, cold_reps):
             cold[name] = (float(np.median(ts)), float(np.min(ts)))
         del evict
         torch.cuda.empty_cache()  # later buffers (the probe's) get memory of their own
-    return wall, per, cold
+    return wall, dev_ms, per, cold
 
 
 def time_windows(fn, reps=20, warmup=20, windows=5):
@@ -465,12 +467,12 @@ def bench_moe(args) -> int:
         torch.cuda.empty_cache()
 
     log(f"{op}: warm-up {args.warmup}, timing {args.steps} steps")
-    wall, per, cold = time_kernels(kernels, args.steps, args.warmup, args.cold_reps)
+    wall, dev_ms, per, cold = time_kernels(kernels, args.steps, args.warmup, args.cold_reps)
     total = sum(nbytes.values())
     value = total / (wall * 1e6)
     kern = {}
     for name, _ in kernels:
-        avg = float(np.mean(per[name]))
+        avg = per[name]
         kern[name] = {"algorithmic_bytes": nbytes[name], "us": round(avg * 1e3, 2),
                       "GB/s": round(nbytes[name] / (avg * 1e6), 1),
                       "frac_of_peak": round(nbytes[name] / (avg * 1e6) / HBM_PEAK_GBS, 4)}
@@ -490,47 +492,50 @@ def bench_moe(args) -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle
         import oracle.moe as mo
         orc = mo.get()
-        # a bounded sample: the oracle on a leading slice of the same inputs, ~cpu_seconds
-        frac = {"residual_add": 1.0, "router_weight": 0.125, "squared_relu": 0.25, "unpermute": 0.25}[op]
+        threads = oracle.default_threads()
+        # the oracle on the whole of the same inputs (each op's full batch runs in about a
+        # second on a GPU's share of host cores), repeated up to ~cpu_seconds
         spent, reps, moved = 0.0, 0, 0
         while reps < 1 or (spent < args.cpu_seconds and reps < 50):
             t = time.perf_counter()
             if op == "residual_add":
-                orc.residual_add(inp["expert"], inp["shared"], inp["residual"], "bf16")
-                moved += total
+                orc.residual_add(inp["expert"], inp["shared"], inp["residual"], "bf16", threads=threads)
             elif op == "router_weight":
-                n = int(inp["x"].shape[0] * frac)
-                orc.router_weight_fwd(inp["x"][:n], "bf16", inp["probs"][:n], "bf16")
-                orc.router_weight_bwd(inp["grad_out"][:n], "bf16", inp["x"][:n], "bf16", inp["probs"][:n])
-                moved += int(total * n / inp["x"].shape[0])
+                orc.router_weight_fwd(inp["x"], "bf16", inp["probs"], "bf16", threads=threads)
+                orc.router_weight_bwd(inp["grad_out"], "bf16", inp["x"], "bf16", inp["probs"],
+                                      threads=threads)
             elif op == "squared_relu":
-                n = int(inp["x"].shape[0] * frac)
-                orc.squared_relu_probs(inp["x"][:n], inp["probs"][:n], clamp_scale=inp["clamp_scale"])
-                orc.squared_relu_probs_bwd(inp["x"][:n], inp["probs"][:n], inp["grad_y"][:n],
-                                           clamp_scale=inp["clamp_scale"])
-                moved += int(total * n / inp["x"].shape[0])
+                orc.squared_relu_probs(inp["x"], inp["probs"], clamp_scale=inp["clamp_scale"],
+                                       threads=threads)
+                orc.squared_relu_probs_bwd(inp["x"], inp["probs"], inp["grad_y"],
+                                           clamp_scale=inp["clamp_scale"], threads=threads)
             else:
-                n = int(inp["inverse_map"].shape[0] * frac)
-                orc.unpermute(inp["expert_output"], inp["inverse_map"][:n], "f32")
-                moved += int(total * n / inp["inverse_map"].shape[0])
+                orc.unpermute(inp["expert_output"], inp["inverse_map"], "f32", threads=threads)
+            moved += total
             spent += time.perf_counter() - t
             reps += 1
-        cpu = {"value": round(moved / (spent * 1e9), 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{'all' if frac == 1.0 else f'the first {frac:g} of the'} rows of the same "
-                         f"inputs x {reps} reps, {spent:.1f} s; {cpu_model()}"}
+        cpu = {"value": round(moved / (spent * 1e9), 3), "unit": "GB/s", "cores": threads,
+               "host_cores": oracle.host_cores(), "kind": "oracle",
+               "sample": (f"the full batch of the same inputs x {reps} reps, {spent:.1f} s, on "
+                          f"{threads} threads (OMP_NUM_THREADS caps the host's cores to this GPU's "
+                          f"share); {cpu_model()}")}
         log(f"{op}: cpu baseline {cpu['value']} GB/s")
 
     print(json.dumps({
         "metric": f"achieved HBM GB/s of the {MOE_OPS[op]} and % of MI355X HBM peak",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(wall, 5), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(wall, 5), "device_ms_per_step": round(dev_ms, 5),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"moe_{op}", **shape, "io_dtype": "bf16", "seed": 0},
         "kernels": kern,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": kern[dom]["frac_of_peak"], "traffic": traffic},
+                     "unit": "GB/s", "frac": kern[dom]["frac_of_peak"], "traffic": traffic,
+                     "timing": "the kernel alone, launched back to back (median of five windows of "
+                               "20 launches, as the probe)"},
         "hbm_probe": probe,
         "cpu_baseline": cpu,
     }), flush=True)

@@ -58,6 +58,17 @@ def _same(a, b, dt):
     return bool(np.all((a == b) | (na & nb)))
 
 
+def _same_by_rows(got, want, dt, what, block=4096):
+    """_same over row blocks (bounds the temporaries at the full workload sizes)."""
+    for r in range(0, got.shape[0], block):
+        assert _same(got[r:r + block], want[r:r + block], dt), f"{what}: rows {r}..{r + block} differ"
+
+
+def _within_ulp_by_rows(got, want, what, block=4096):
+    for r in range(0, got.shape[0], block):
+        assert_within_ulp(got[r:r + block], want[r:r + block], 1, f"{what} rows {r}..")
+
+
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("n", [1, 7, 8, 1000, 4096 * 7 + 5, 1 << 22])
@@ -212,9 +223,10 @@ def test_router_weight_autograd_and_grid():
         assert torch.equal(o, outs[0][0]) and torch.equal(gp.view(torch.int32), outs[0][1].view(torch.int32))
 
 
-def test_router_weight_full_size_sampled():
+def test_router_weight_full_size():
     """53760 x 7168 bf16 (the MoE workload), default launch (the backward's waves take
-    quarter rows): sampled rows against the oracle, forward and grad_x bitwise."""
+    quarter rows): every row against the oracle, forward and grad_x bitwise, every
+    grad_probs row on the row-scale criterion."""
     from memory_bound_elementwise_amd.workloads import make_moe_inputs
     inp = make_moe_inputs("router_weight", seed=0)
     x, p, g = inp["x"], inp["probs"], inp["grad_out"]
@@ -227,14 +239,12 @@ def test_router_weight_full_size_sampled():
     moe_router_weight_fwd(xd, dp, out)
     moe_router_weight_bwd(gd, xd, dp, gx, gp)
     torch.cuda.synchronize()
-    idx = np.unique(np.concatenate([np.arange(3), np.arange(tokens - 100, tokens),
-                                    np.random.default_rng(3).integers(0, tokens, 200)]))
-    ti = torch.from_numpy(idx).to(DEV)
     orc = moe_oracle.get()
-    assert _same(_host(out[ti], "bf16"), orc.router_weight_fwd(x[idx], "bf16", p[idx], "bf16"), "bf16")
-    ref = orc.router_weight_bwd(g[idx], "bf16", x[idx], "bf16", p[idx])
-    assert _same(_host(gx[ti], "bf16"), ref["grad_x"], "bf16")
-    bad = grad_probs_violations(gp[ti].cpu().numpy(), ref["grad_probs_f64"], ref["row_scale"])
+    _same_by_rows(_host(out, "bf16"), orc.router_weight_fwd(x, "bf16", p, "bf16"), "bf16", "router fwd")
+    del out
+    ref = orc.router_weight_bwd(g, "bf16", x, "bf16", p)
+    _same_by_rows(_host(gx, "bf16"), ref["grad_x"], "bf16", "router grad_x")
+    bad = grad_probs_violations(gp.cpu().numpy(), ref["grad_probs_f64"], ref["row_scale"])
     assert bad.size == 0, f"router grad_probs: {bad.size} rows off"
 
 
@@ -294,8 +304,8 @@ def test_squared_relu_rows(zero_padding):
 
 
 @pytest.mark.parametrize("clamp_scale", [None, 4.0])
-def test_squared_relu_full_size_sampled(clamp_scale):
-    """53,760 x 2,048 (the MoE workload), default launch; sampled rows against the oracle."""
+def test_squared_relu_full_size(clamp_scale):
+    """53,760 x 2,048 (the MoE workload), default launch; every row against the oracle."""
     from memory_bound_elementwise_amd.workloads import make_moe_inputs
     inp = make_moe_inputs("squared_relu", seed=0)
     x, p = inp["x"], inp["probs"]
@@ -304,14 +314,12 @@ def test_squared_relu_full_size_sampled(clamp_scale):
     y = torch.empty((rows, hidden), dtype=torch.bfloat16, device=DEV)
     moe_squared_relu_probs_fwd(_dev(x, "bf16"), torch.from_numpy(p).to(DEV), y, clamp_scale=clamp_scale)
     torch.cuda.synchronize()
-    idx = np.unique(np.concatenate([np.arange(3), np.arange(rows - 200, rows),
-                                    np.random.default_rng(4).integers(0, rows, 300)]))
-    got = _host(y[torch.from_numpy(idx).to(DEV)], "bf16")
-    want = moe_oracle.get().squared_relu_probs(x[idx], p[idx], clamp_scale=clamp_scale)
+    got = _host(y, "bf16")
+    want = moe_oracle.get().squared_relu_probs(x, p, clamp_scale=clamp_scale)
     if clamp_scale is None:
-        assert _same(got, want, "bf16")
+        _same_by_rows(got, want, "bf16", "full size")
     else:
-        assert_within_ulp(got, want, 1, "full size")
+        _within_ulp_by_rows(got, want, "full size")
 
 
 # ---------------------------------------------------------------------------
@@ -452,26 +460,26 @@ def test_squared_relu_autograd(clamp_scale):
 
 
 @pytest.mark.parametrize("clamp_scale", [None, 4.0])
-def test_squared_relu_bwd_full_size_sampled(clamp_scale):
-    """53,760 x 2,048 (the MoE workload), default launch; sampled rows against the oracle."""
+def test_squared_relu_bwd_full_size(clamp_scale):
+    """53,760 x 2,048 (the MoE workload), default launch; every row against the oracle."""
     from memory_bound_elementwise_amd.workloads import make_moe_inputs
     inp = make_moe_inputs("squared_relu", seed=0)
-    x, p = inp["x"], inp["probs"]
+    x, p, gys = inp["x"], inp["probs"], inp["grad_y"]
     rows, hidden = x.shape
-    g = torch.Generator(device=DEV).manual_seed(9)
-    gy = torch.randn(rows, hidden, device=DEV, generator=g).to(torch.bfloat16)
+    gy = _dev(gys, "bf16")
     xd = _dev(x, "bf16")
     gx = torch.empty_like(xd)
     gp = torch.full((rows,), GP_SENTINEL, device=DEV)
     say(f"[sqrelu bwd full] s={clamp_scale} {rows}x{hidden}")
     moe_squared_relu_probs_bwd(xd, torch.from_numpy(p).to(DEV), gy, gx, gp, clamp_scale=clamp_scale)
     torch.cuda.synchronize()
-    idx = np.unique(np.concatenate([np.arange(3), np.arange(rows - 200, rows),
-                                    np.random.default_rng(1).integers(0, rows, 300)]))
-    ti = torch.from_numpy(idx).to(DEV)
-    gys = _host(gy[ti], "bf16")
-    want = moe_oracle.get().squared_relu_probs_bwd(x[idx], p[idx], gys, clamp_scale=clamp_scale)
-    _check_sqb(_host(gx[ti], "bf16"), gp[ti].cpu().numpy(), want, clamp_scale, "full size")
+    want = moe_oracle.get().squared_relu_probs_bwd(x, p, gys, clamp_scale=clamp_scale)
+    got = _host(gx, "bf16")
+    if clamp_scale is None:
+        _same_by_rows(got, want["grad_x"], "bf16", "full size grad_x")
+    else:
+        _within_ulp_by_rows(got, want["grad_x"], "full size grad_x")
+    _check_grad_probs(gp.cpu().numpy(), want, "full size")
 
 
 # ---------------------------------------------------------------------------
@@ -536,9 +544,9 @@ def test_unpermute_grid_invariant(E):
 
 
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
-def test_unpermute_full_size_sampled(out_dt):
-    """6720 tokens x 8 local experts x 7168 (the MoE workload), default launch; sampled
-    tokens against the oracle on the rows they gather."""
+def test_unpermute_full_size(out_dt):
+    """6720 tokens x 8 local experts x 7168 (the MoE workload), default launch; every
+    token against the oracle, bitwise."""
     from memory_bound_elementwise_amd.workloads import make_moe_inputs
     inp = make_moe_inputs("unpermute", seed=0)
     eo, im = inp["expert_output"], inp["inverse_map"]
@@ -547,10 +555,8 @@ def test_unpermute_full_size_sampled(out_dt):
     out = torch.empty((tokens, hidden), dtype=TD[out_dt], device=DEV)
     moe_unpermute_expert_order(_dev(eo, "bf16"), torch.from_numpy(im).to(DEV), out)
     torch.cuda.synchronize()
-    idx = np.unique(np.concatenate([np.arange(3), np.arange(tokens - 100, tokens),
-                                    np.random.default_rng(2).integers(0, tokens, 300)]))
-    want = moe_oracle.get().unpermute(eo, im[idx], out_dt)
-    assert _same(_host(out, out_dt)[idx], want, out_dt)
+    want = moe_oracle.get().unpermute(eo, im, out_dt)
+    _same_by_rows(_host(out, out_dt), want, out_dt, "unpermute")
 
 
 def test_unpermute_order_and_bound():

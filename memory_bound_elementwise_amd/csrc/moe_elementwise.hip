@@ -11,11 +11,13 @@
 // All are streams built on cdna4_stream.h: 128-bit buffer accesses on per-row (or
 // per-block) resources whose hardware range check masks ragged ends and rows that
 // are not live, nontemporal hints, and the two-buffer software pipeline per wave.
-// Grids follow the shared rules (walk_workgroups / split_walk_workgroups): one wave
-// per row or 2 KiB block for short rows, rows of 4 or more chunks shared by a
-// workgroup's four waves (router weight), one persistent workgroup per CU for the
-// pipelined unpermute. The soft-clamped squared ReLU, the one op the vector ALU
-// rather than HBM bounds, always runs one wave per row. Values are handled in groups
+// Default grids: one wave per 2 KiB block (residual add), rows of 4 or more chunks
+// shared by a workgroup's four waves (router weight), one wave per row of at most two
+// chunks, loaded whole (squared ReLU, both directions), and one wave per (token,
+// column chunk) gathering only the contributing experts' rows (unpermute, up to 8
+// local experts). Other shapes, and launches with an explicit workgroup count, take
+// the fixed-grid walks (walk_workgroups / split_walk_workgroups; a persistent
+// pipelined walk for the unpermute), with the same bits. Values are handled in groups
 // of eight elements per lane ("octs": one 16-byte access for 16-bit types, two for
 // fp32).
 #include <hip/hip_runtime.h>

@@ -25,8 +25,9 @@
 //     all loads issued at once); the backward gives each wave one whole row of up to
 //     3 vectors per lane, and splits rows of exactly 4 chunks among the four waves of
 //     a workgroup, one chunk each (the 2,048- and 4,096-column rows). The row's slot
-//     and probability come from scalar loads, so a wave carries no per-row bookkeeping
-//     beyond its own row.
+//     comes from scalar loads (n_used, the map entry) and its probability from a
+//     one-dword buffer load issued with the row's streaming loads, so a wave carries no
+//     per-row bookkeeping beyond its own row.
 //   * Other shapes, and launches with an explicit workgroup count, run the fixed-grid
 //     walks of cdna4_stream.h: waves (or workgroups, for shared rows) stride over
 //     rows (row r, r + W, r + 2W, ...), each wave pipelining the loads of its next

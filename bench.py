@@ -31,7 +31,8 @@ Printed JSON line (stdout):
                no input can come from the previous launch's cache state; median and
                minimum of --cold-reps launches (default 30)
   hbm_probe    streaming ceilings at the same bytes: the in-repo probe (1:1 copy, 2:1 and
-               3:2 read:write) and, sharing no code with the kernels, torch copy_, a bf16
+               3:2 read:write, read-only over three arrays, write-only over two) and,
+               sharing no code with the kernels, torch copy_, a bf16
                torch.add and hipMemcpyDtoDAsync. With --op, the probe at each kernel's
                own read:write mix and size, and the kernel's fraction of it
 With --op (a MoE operation), the step is that op's kernels in order; kernels.<name>.us is
@@ -302,11 +303,16 @@ def streaming_ceilings(n_elems, dev):
         if rc != 0:
             raise RuntimeError(f"hipMemcpyDtoDAsync failed: hipError_t {rc}")
 
-    from memory_bound_elementwise_amd.hbm_probe import hbm_probe_stream
+    from memory_bound_elementwise_amd.hbm_probe import hbm_probe_fill, hbm_probe_read, hbm_probe_stream
+    sink = torch.empty(4, dtype=torch.int32, device=dev)
     cases = [
         ("copy_1r1w", "in-repo probe", lambda: hbm_probe_stream(i16[:1], i16[3:4]), 2),
         ("fwd_like_2r1w", "in-repo probe", lambda: hbm_probe_stream(i16[:2], i16[3:4]), 3),
         ("bwd_like_3r2w", "in-repo probe", lambda: hbm_probe_stream(i16[:3], i16[3:5]), 5),
+        # the two ends of the read:write range (the sources hold bf16 1.0, 0x3f80 per
+        # half-word, whose XOR over three arrays is never the key)
+        ("read_only_3r", "in-repo probe", lambda: hbm_probe_read(i16[:3], 0xFFFFFFFF, sink), 3),
+        ("write_only_2w", "in-repo probe", lambda: hbm_probe_fill(i16[3:5], 0x3F803F80), 2),
         ("torch_copy_1r1w", "torch Tensor.copy_", lambda: bufs[3].copy_(bufs[0]), 2),
         ("torch_add_2r1w", "torch.add (bf16)", lambda: torch.add(bufs[0], bufs[1], out=bufs[3]), 3),
         ("hip_memcpy_1r1w", "hipMemcpyDtoDAsync", memcpy, 2),
@@ -319,7 +325,7 @@ def streaming_ceilings(n_elems, dev):
                      "GB/s": round(moved / (ms * 1e6), 1),
                      "frac_of_peak": round(moved / (ms * 1e6) / HBM_PEAK_GBS, 4)}
         log(f"ceiling {name} ({kind}): {out[name]['GB/s']} GB/s")
-    del bufs, i16
+    del bufs, i16, sink
     torch.cuda.empty_cache()
     return out
 

@@ -33,6 +33,29 @@ extern "C" {
 int hbm_probe_stream(const void *const *src, int n_src, void *const *dst, int n_dst,
                      int64_t n_vec, int num_workgroups, hipStream_t stream);
 
+/*
+ * One-way streams, the two ends of the read:write range, with the same access pattern,
+ * grid and limits as hbm_probe_stream.
+ *
+ * hbm_probe_read reads n_src (1..3) arrays of n_vec 16-byte vectors and writes nothing
+ * in practice: each lane keeps the XOR of the vectors it read and stores it to `sink`
+ * (one 16-byte device buffer, 16-byte aligned, not inside a source) only where all four
+ * of its 32-bit words equal `key`. Pick a key the data cannot produce (with every source
+ * holding one repeated word w, an odd count of sources gives w, an even count 0); the
+ * conditional store only keeps the loads from being dropped. A lane's XOR covers the
+ * vectors it read, so which lanes match depends on the grid.
+ *
+ * hbm_probe_fill writes `value` to every 32-bit word of n_dst (1..2) arrays of n_vec
+ * 16-byte vectors (non-overlapping), reading nothing.
+ *
+ * Return codes as hbm_probe_stream.
+ */
+int hbm_probe_read(const void *const *src, int n_src, int64_t n_vec, uint32_t key, void *sink,
+                   int num_workgroups, hipStream_t stream);
+
+int hbm_probe_fill(void *const *dst, int n_dst, int64_t n_vec, uint32_t value, int num_workgroups,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -149,6 +149,36 @@ def test_probe_validation(built):
     assert so.hbm_probe_stream(s, 1, d, 1, 2 ** 63 - 1, 0, None) == 1
 
 
+def test_probe_one_way_validation(built):
+    """The read-only and write-only streams check their arguments before any launch."""
+    so = ctypes.CDLL(mbuild.lib_path("hbm_probe"))
+    so.hbm_probe_read.restype = so.hbm_probe_fill.restype = ctypes.c_int
+    so.hbm_probe_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    so.hbm_probe_fill.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+    s = (ctypes.c_void_p * 3)(A16, A16 + (1 << 24), A16 + (2 << 24))
+    sink = A16 + (3 << 24)
+    assert so.hbm_probe_read(s, 3, 0, 7, sink, 0, None) == 0           # empty: no launch
+    assert so.hbm_probe_read(s, 0, 4, 7, sink, 0, None) == 1
+    assert so.hbm_probe_read(s, 4, 4, 7, sink, 0, None) == 1
+    assert so.hbm_probe_read(s, 1, 4, 7, None, 0, None) == 1            # no sink
+    assert so.hbm_probe_read(s, 1, 4, 7, sink + 8, 0, None) == 1        # misaligned sink
+    assert so.hbm_probe_read(s, 1, 4, 7, A16 + 16, 0, None) == 1        # sink inside a source
+    assert so.hbm_probe_read(s, 1, -1, 7, sink, 0, None) == 1
+    assert so.hbm_probe_read(s, 1, (1 << 44) + 1, 7, sink, 0, None) == 1
+    assert so.hbm_probe_read(s, 1, 4, 7, sink, 1 << 24, None) == 1
+    bad = (ctypes.c_void_p * 1)(A16 + 4)
+    assert so.hbm_probe_read(bad, 1, 4, 7, sink, 0, None) == 1
+    d = (ctypes.c_void_p * 2)(A16, A16 + 32)
+    assert so.hbm_probe_fill(d, 1, 0, 7, 0, None) == 0                  # empty: no launch
+    assert so.hbm_probe_fill(d, 0, 4, 7, 0, None) == 1
+    assert so.hbm_probe_fill(d, 3, 4, 7, 0, None) == 1
+    assert so.hbm_probe_fill(d, 2, 4, 7, 0, None) == 1                  # the two overlap
+    assert so.hbm_probe_fill(bad, 1, 4, 7, 0, None) == 1
+    assert so.hbm_probe_fill(d, 1, 2 ** 63 - 1, 7, 0, None) == 1
+
+
 def test_moe_validation():
     from memory_bound_elementwise_amd.moe_elementwise import load_library as load_moe
     lib = load_moe()

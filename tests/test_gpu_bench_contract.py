@@ -47,8 +47,8 @@ def test_headline_line():
     assert d["roofline"]["kernel"] == "swiglu_probs_bwd"
     assert d["fwd"]["algorithmic_bytes"] == 660817920 and d["bwd"]["algorithmic_bytes"] == 1101434880
     assert abs(d["roofline"]["achieved"] - d["bwd"]["GB/s"]) < 0.2
-    assert set(d["hbm_probe"]) == {"copy_1r1w", "fwd_like_2r1w", "bwd_like_3r2w", "torch_copy_1r1w",
-                                   "torch_add_2r1w", "hip_memcpy_1r1w"}
+    assert set(d["hbm_probe"]) == {"copy_1r1w", "fwd_like_2r1w", "bwd_like_3r2w", "read_only_3r",
+                                   "write_only_2w", "torch_copy_1r1w", "torch_add_2r1w", "hip_memcpy_1r1w"}
     for name in ("fwd", "bwd"):
         k = d[name]
         # each launch's own start/end events: the durations are those of the kernel alone

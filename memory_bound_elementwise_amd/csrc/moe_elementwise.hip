@@ -1138,10 +1138,14 @@ constexpr int kUnpermuteBlocksPerCU = 2;
 constexpr int kUnpermutePipelinedMaxExperts = 8;
 constexpr int kUnpermutePipeU = 2;
 constexpr int kUnpermutePipeBlocksPerCU = 1;
-// Octs per lane per chunk of the one-unit-per-wave unpermute.
-constexpr int kUnpermuteUnitU = 2;
-// The soft-clamped squared ReLU (forward ~19, backward ~30 vector instructions per
-// element) keeps the VALU 73% / 86% busy. It runs with 2 octs per lane per chunk
+// Octs per lane per chunk of the one-unit-per-wave unpermute, by output type. At 6,720
+// tokens x 8 experts x 7,168 (medians of five windows, interleaved builds): fp32 out
+// 91.4 us at 1, 94.5 at 2, 97.8 at 4; bf16 out 80.4, 79.5, 81.8. The bits do not
+// depend on it.
+template <int ODT>
+constexpr int kUnpermuteUnitU = ODT == DT_F32 ? 1 : 2;
+// The soft-clamped squared ReLU (forward ~16, backward ~31 vector instructions per
+// element) keeps the VALU 61% / 84% busy. It runs with 2 octs per lane per chunk
 // (83 registers, up to 6 waves per SIMD) and one wave per row whatever the row length.
 // Measured at 53760 x 2048: forward 72.6 us and backward 103.8 us, level with the
 // unclamped kernels, against 81.9 / 118.9 us with a balanced grid of 1920
@@ -1459,20 +1463,21 @@ moe_status_t moe_unpermute_expert_order(const uint16_t *expert_output, int64_t e
     hipError_t he = device_cus(&cus);
     if (he != hipSuccess)
         return fail_hip(he);
-    const int64_t units = tokens * row_chunks(hidden / 8, kUnpermuteUnitU);
+    const int unit_u = out_dtype == MOE_FP32 ? kUnpermuteUnitU<DT_F32> : kUnpermuteUnitU<DT_BF16>;
+    const int64_t units = tokens * row_chunks(hidden / 8, unit_u);
     if (num_workgroups == 0 && num_local_experts <= 8 &&
         (units + kWavesPerBlock - 1) / kWavesPerBlock <= kMaxWorkgroups && units <= 0x7fffffffLL) {
         const int blocks = (int)((units + kWavesPerBlock - 1) / kWavesPerBlock);
-        const int nch = (int)row_chunks(hidden / 8, kUnpermuteUnitU);
+        const int nch = (int)row_chunks(hidden / 8, unit_u);
         char *o = static_cast<char *>(out);
         if (out_dtype == MOE_FP32)
-            hipLaunchKernelGGL((unpermute_unit_kernel<DT_F32, kUnpermuteUnitU>), dim3(blocks), dim3(kBlock), 0, stream,
-                               (int)tokens, (int)hidden, num_local_experts, nch, (int)expert_rows, expert_output,
-                               inverse_map, o, valid_tokens);
+            hipLaunchKernelGGL((unpermute_unit_kernel<DT_F32, kUnpermuteUnitU<DT_F32>>), dim3(blocks), dim3(kBlock), 0,
+                               stream, (int)tokens, (int)hidden, num_local_experts, nch, (int)expert_rows,
+                               expert_output, inverse_map, o, valid_tokens);
         else
-            hipLaunchKernelGGL((unpermute_unit_kernel<DT_BF16, kUnpermuteUnitU>), dim3(blocks), dim3(kBlock), 0, stream,
-                               (int)tokens, (int)hidden, num_local_experts, nch, (int)expert_rows, expert_output,
-                               inverse_map, o, valid_tokens);
+            hipLaunchKernelGGL((unpermute_unit_kernel<DT_BF16, kUnpermuteUnitU<DT_BF16>>), dim3(blocks), dim3(kBlock), 0,
+                               stream, (int)tokens, (int)hidden, num_local_experts, nch, (int)expert_rows,
+                               expert_output, inverse_map, o, valid_tokens);
         return launched();
     }
     const bool pipelined = num_local_experts <= kUnpermutePipelinedMaxExperts;

@@ -323,6 +323,44 @@ __device__ __forceinline__ float row_sum_split(float (*part)[kWave], float acc, 
     return t;
 }
 
+// The same row total for a workgroup that handles one row, without a barrier at the
+// end: each wave writes its partials to part[w] and counts itself in `arrived`; the
+// wave that arrives last (whichever it is) adds the partials of waves 0, 1, 2, 3 in that
+// order and reduces them with wave_sum, exactly as row_sum_split does, and returns true
+// with the total. The others return false at once instead of waiting for the slowest
+// wave's loads. `arrived` must be zero and visible to every wave first:
+// row_sum_last_init, called by every wave (it holds a barrier) before any wave can
+// arrive; early in the kernel the four waves reach it together. The fences are on LDS
+// alone, so global accesses in flight are not waited for.
+__device__ __forceinline__ void row_sum_last_init(unsigned *arrived, int w, int lane)
+{
+    if (w == 0 && lane == 0)
+        *arrived = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ bool row_sum_last(float (*part)[kWave], unsigned *arrived, float acc, int w, int lane,
+                                             float &total)
+{
+    part[w][lane] = acc;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    unsigned before = 0u;
+    if (lane == 0)
+        before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != kWavesPerBlock - 1)
+        return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    float t = part[0][lane];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i)
+        t += part[i][lane];
+    total = wave_sum(t);
+    return true;
+}
+
 // One row per wave (row = the wave's index in the grid), all `NCH` column chunks of it
 // loaded at once, for the default launch of rows of at most a couple of chunks: no walk,
 // no per-row bookkeeping beyond the row's own slot (row_slot) and probability

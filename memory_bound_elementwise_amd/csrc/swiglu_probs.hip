@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_row_kernel(
 // of U vectors per lane, wave w taking chunk w. The row sum goes through row_sum_last:
 // walk_row_split's order for a row of four chunks, with no barrier at the end (the
 // slowest wave of the row does the sum; the others leave). At 53760 x 2048 (medians of
-// eight interleaved rounds): 172.2 against 172.7 us with row_sum_split's end-of-row
+// twelve interleaved rounds): 172.0 against 172.7 us with row_sum_split's end-of-row
 // barrier; with no row sum at all (grad_probs NULL) the backward takes about 0.9% less.
 template <int U>
 __global__ __launch_bounds__(kBlock) void swiglu_probs_bwd_quarter_kernel(

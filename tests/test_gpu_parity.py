@@ -83,10 +83,21 @@ def test_row_subset_invariance():
     assert np.array_equal(got[2].view(np.uint32), ref[2][sub].view(np.uint32))
 
 
-def test_no_grad_probs_pointer():
-    """grad_probs = NULL skips the reduction and leaves grad_x unchanged."""
-    inp = make_inputs("tiny", seed=4)
+@pytest.mark.parametrize("inter", [256, 2048, 4096])
+def test_no_grad_probs_pointer(inter):
+    """grad_probs = NULL skips the reduction and leaves grad_x unchanged. At 2,048 and
+    4,096 columns the default launch is the quarter-row kernel, whose row-sum barrier is
+    taken only for live rows with a grad_probs pointer: padding rows, dummy rows and a
+    NULL pointer must all go through without it."""
+    from memory_bound_elementwise_amd.workloads import Workload
+    w = Workload("nogp", rows=700, inter=inter, limit=7.0, x_std=3.0, probs="topk_softmax",
+                 n_used=650, permute=True, zero_padding=True)
+    inp = make_inputs(w, seed=inter + 4)
+    pm = inp["permutation_map"].copy()
+    pm[[5, 77, 300]] = -1
+    inp["permutation_map"] = pm
     _, gx_ref, _ = run_gpu(inp, do_fwd=False)
+    check_parity(inp, label=f"no-grad_probs reference inter={inter}")
     _, gx, gp = run_gpu(inp, do_fwd=False, grad_probs=False)
     assert gp is None and np.array_equal(gx, gx_ref)
 

@@ -4,9 +4,10 @@
  * bench's CPU-baseline leg use it. It shares no code with the HIP libraries.
  *
  *   residual add      Megatron-Core "core.fusions.fused_moe_residual_add" page:
- *                     out = residual + (expert_output + shared_expert_output), the
- *                     routed and shared outputs summed and rounded to the activation
- *                     dtype first, so the result equals two unfused adds.
+ *                     out = residual + (expert_output + shared_expert_output). Each
+ *                     of the two additions is done in fp32 and rounded to the element
+ *                     type on its own, inner one first: the bits two separate
+ *                     elementwise additions would give.
  *   router weight     NeMo AutoModel "moe/optimized_ops" page, _RouterWeightMulFunction:
  *                     forward (x.float() * probs.float()).to(out_dtype); backward
  *                     grad_x = (g_f32 * probs_f32).to(x.dtype),

@@ -3,17 +3,18 @@
  * expert activation for AMD Instinct MI355X (gfx950).
  *
  * The operation (NeMo AutoModel "moe/swiglu_triton" page, module docstring and
- * the SwigluClampedTriton class entry): the routed experts' grouped-GEMM output
- * x = [gate | up] (bf16, [rows, 2*inter], gate is the first half) and one fp32
- * routing probability per row give
+ * the SwigluClampedTriton class entry): with x = [gate | up], the bf16 result of the
+ * routed experts' grouped GEMM ([rows, 2*inter], gate in the first half), and one fp32
+ * routing probability per row,
  *
  *     y = silu(clamp(gate, max=L)) * clamp(up, -L, L) * probs
  *
  * computed in fp32 and rounded once to bf16 (round to nearest, ties to even).
- * The backward writes d_gate and d_up straight into the two halves of grad_x and
- * reduces the per-row probability gradient grad_probs = sum_j grad_y * silu(cg) * cu
- * in fp32. Clamp gradients follow torch.clamp: the masks gate <= L and
- * -L <= up <= L are inclusive on the input values.
+ * The backward stores d_gate in the first half of grad_x and d_up in the second (no
+ * separate concatenation) and reduces the per-row probability gradient
+ * grad_probs = sum_j grad_y * silu(cg) * cu in fp32. Clamp gradients follow
+ * torch.clamp: the masks gate <= L and -L <= up <= L are inclusive on the input
+ * values.
  *
  * Row bookkeeping (Megatron-Core "core.inference.moe.batch_invariant" page,
  * _swiglu_with_probs_kernel / swiglu_with_probs / _weighted_silu_mul_bounded_kernel):
@@ -105,8 +106,8 @@ swiglu_status_t swiglu_probs_fwd(const uint16_t *x, const float *probs, uint16_t
                                  int zero_padding, hipStream_t stream);
 
 /*
- * Backward (swiglu_triton page: backward kernel writing d_gate / d_up into the two
- * halves of grad_x and accumulating the per-row probability gradient).
+ * Backward (swiglu_triton page: the one-pass backward kernel, gate and up gradients
+ * stored in place in grad_x, the per-row probability gradient summed as it goes).
  *
  *   x, probs     as in the forward (the forward's saved inputs; nothing else is saved)
  *   grad_y       [rows, inter] bf16 bits, gradient of y

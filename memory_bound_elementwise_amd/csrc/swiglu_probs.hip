@@ -3,7 +3,7 @@
 //
 // What is computed (NeMo AutoModel "moe/swiglu_triton" page, module docstring):
 //   y = silu(clamp(gate, max=L)) * clamp(up, -L, L) * probs, fp32 math, one bf16
-//   rounding; the backward writes d_gate / d_up into the two halves of grad_x and
+//   rounding; the backward stores d_gate / d_up in the gate / up halves of grad_x and
 //   reduces the per-row probability gradient in fp32. Clamp gradients follow
 //   torch.clamp (inclusive masks). Row bookkeeping (n_used, permutation_map,
 //   zero_padding, fixed grid striding over rows) follows the Megatron-Core

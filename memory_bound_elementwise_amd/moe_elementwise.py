@@ -248,8 +248,8 @@ def moe_unpermute_expert_order(expert_output, inverse_map, out, *, valid_tokens=
 
 
 class FusedMoEResidualAdd(torch.autograd.Function):
-    """residual + (expert_output + shared_expert_output) in one kernel; the backward passes the
-    output gradient to all three inputs (they enter the sum with unit weight)."""
+    """residual + (expert_output + shared_expert_output), one fused launch. Each input enters
+    the sum with weight one, so the backward hands the incoming gradient to all of them."""
 
     @staticmethod
     def forward(ctx, expert_output, shared_expert_output, residual):

@@ -13,9 +13,9 @@ a fixed order, so both sides see the same bytes:
 4. workload-specific draws (edge-value masks, zeroed probabilities, router
    logits, the permutation).
 
-The workloads stand in for the one shape the pages name (a "1.1 GB pass at the
-16-node shape" of the routed-expert activation, NeMo AutoModel "moe/swiglu_triton"
-page, module docstring) and for the padded inference layout of the Megatron-Core
+The workloads stand in for the one shape the pages name (one GPU's share of the
+routed-expert activation in a 16-node deployment, whose backward moves about 1.1 GB;
+NeMo AutoModel "moe/swiglu_triton" page, module docstring) and for the padded inference layout of the Megatron-Core
 "core.inference.moe.batch_invariant" page (swiglu_with_probs: permutation_map,
 n_used, zero_padding). Arrays are numpy: bf16 values as uint16 bit patterns,
 probabilities fp32, the map int32.

@@ -9,9 +9,9 @@
  *                     type on its own, inner one first: the bits two separate
  *                     elementwise additions would give.
  *   router weight     NeMo AutoModel "moe/optimized_ops" page, _RouterWeightMulFunction:
- *                     forward (x.float() * probs.float()).to(out_dtype); backward
- *                     grad_x = (g_f32 * probs_f32).to(x.dtype),
- *                     grad_probs = (g_f32 * x_f32).sum(-1) in fp32.
+ *                     forward: out = x * p per row, one fp32 product rounded to the
+ *                     output type; backward: grad_x = g * p, one fp32 product rounded
+ *                     to x's type, and grad_p = the row sum of g * x in fp32.
  *   squared ReLU      Megatron-Core "core.inference.moe.batch_invariant" page,
  *                     _squared_relu_with_probs_kernel / squared_relu_with_probs:
  *                     with the soft clamp, c = s * tanh(x / s), relu(c)^2 * p all in

@@ -17,7 +17,9 @@ Printed JSON line (stdout):
   fwd, bwd     per-kernel duration over K more steps run right after the timed ones, in
                which each launch records its own start and end into a pair of events
                (the library's timed entry points, hipExtLaunchKernel): the kernel alone;
-               average, min, max, and the GB/s and HBM fraction the average gives. us_back_to_back: the kernel alone, launched
+               average, min, median, max, and the GB/s and HBM fraction the average
+               gives (the roofline uses the average; a few slow launches move it, the
+               median much less). us_back_to_back: the kernel alone, launched
                back to back (median of five windows of 20 launches between one pair of
                stream events); frac_of_best_ceiling: its GB/s over the best ceiling
                measured at its read:write mix
@@ -632,7 +634,8 @@ def main() -> int:
         t = per[name]
         avg = float(np.mean(t))
         res[name] = {"algorithmic_bytes": nbytes[name], "us": round(avg * 1e3, 2),
-                     "us_min": round(min(t) * 1e3, 2), "us_max": round(max(t) * 1e3, 2),
+                     "us_min": round(min(t) * 1e3, 2), "us_median": round(float(np.median(t)) * 1e3, 2),
+                     "us_max": round(max(t) * 1e3, 2),
                      "GB/s": round(nbytes[name] / (avg * 1e6), 1),
                      "frac_of_peak": round(nbytes[name] / (avg * 1e6) / HBM_PEAK_GBS, 4)}
     log(f"fwd {res['fwd']['us']} us ({res['fwd']['GB/s']} GB/s), bwd {res['bwd']['us']} us "

@@ -53,6 +53,7 @@ def test_headline_line():
         k = d[name]
         # each launch's own start/end events: the durations are those of the kernel alone
         assert 0 < k["us_min"] <= k["us"] <= k["us_max"] and k["us_back_to_back"] > 0
+        assert k["us_min"] <= k["us_median"] <= k["us_max"]
         assert 0 < k["frac_of_best_ceiling"] < 1.5
     assert d["device_ms_per_step"] > 0 and d["cold"]["reps"] == 2
     assert d["cpu_baseline"]["host_cores"] >= d["cpu_baseline"]["cores"]
